@@ -1,0 +1,270 @@
+"""Benchmark one paged-attention layer-step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one pass of the whole hot path over one batch: pa_kv_append of the
+step's new tokens, split-K pa_decode, pa_decode_splitk_reduce, and for the
+mixed workload (config 5) pa_prefill_chunk.  Inputs are resident in HBM
+before timing starts.  The pool of every step is a different layer copy
+(rotating over R copies, R * pool >= 1 GiB), so each step reads its KV from
+HBM rather than from the 256 MB Infinity Cache, as a real layer-step does.
+
+Prints one JSON line: the headline metric is KV GB/s of the whole step
+(logical KV bytes read / step time), with us per layer-step, the fraction of
+the 8 TB/s HBM peak, per-kernel HIP-event durations, the roofline of the
+decode kernel and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode KV GB/s (% of HBM peak) + µs per layer-step, 1×MI355X"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_PS = {1: 64, 2: 256, 3: 256, 4: 512, 5: 256}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the paged-attention path here is built and timed on "
+              "a single MI355X (no sharding, no collectives); --gpus %d is not supported"
+              % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_splitk_reduce,
+                                        pa_prefill_chunk, pa_selftest)
+    from workloads import make_config
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    pa_selftest()
+    w = make_config(args.config, seed=args.seed, device=dev)
+    ps = args.partition_size or DEFAULT_PS[args.config]
+
+    def i32(a):
+        return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
+
+    # ---- resident inputs ---------------------------------------------------
+    R = max(2, math.ceil((1 << 30) / w.pool_bytes()))
+    pools = []
+    fill_slots = i32(w.fill_slots)
+    for _ in range(R):
+        p = KVPool(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device=dev,
+                   poison=False, k_scale=w.k_scale, v_scale=w.v_scale)
+        p.append(w.fill_k, w.fill_v, fill_slots)
+        pools.append(p)
+    new_k, new_v = w.new_k.contiguous(), w.new_v.contiguous()
+    new_slots = i32(w.new_slots)
+    q = w.q.contiguous()
+    B, hq, d = q.shape
+    lens, bt = i32(w.context_lens), i32(w.block_tables)
+    pmax = w.max_partitions(ps)
+    part_max = torch.empty((B, hq, pmax), device=dev)
+    part_sum = torch.empty((B, hq, pmax), device=dev)
+    part_out = torch.empty((B, hq, pmax, d), device=dev)
+    out = torch.empty_like(q)
+    has_prefill = w.num_chunks > 0
+    if has_prefill:
+        qp = w.q_prefill.contiguous()
+        outp = torch.empty_like(qp)
+        qsl = i32(w.query_start_loc)
+        maxq = int(np.max(np.diff(w.query_start_loc)))
+        cbt, clens = i32(w.chunk_block_tables), i32(w.chunk_context_lens)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(layer, ev=None):
+        pool = pools[layer % R]
+        if ev is not None:
+            ev[0].record(stream)
+        pool.append(new_k, new_v, new_slots)
+        if ev is not None:
+            ev[1].record(stream)
+        pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
+                  partition_size=ps, max_partitions=pmax, part_max=part_max, part_sum=part_sum,
+                  part_out=part_out)
+        if ev is not None:
+            ev[2].record(stream)
+        pa_decode_splitk_reduce(out, part_max, part_sum, part_out, lens, ps)
+        if ev is not None:
+            ev[3].record(stream)
+        if has_prefill:
+            pa_prefill_chunk(outp, qp, qsl, maxq, pool.k, pool.v, cbt, clens, w.scale,
+                             pool.k_scale, pool.v_scale)
+            if ev is not None:
+                ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ------------------------------------
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-kernel durations (HIP events on the launch stream) -------------
+    nev = 5 if has_prefill else 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    names = ["kv_append", "decode", "splitk_reduce", "prefill_chunk"][:nev - 1]
+    kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+               for j, n in enumerate(names)}
+
+    # ---- accounting -----------------------------------------------------------
+    kv_logical = w.decode_kv_bytes_logical()
+    kv_unique = w.decode_kv_bytes_unique()
+    step_bytes = kv_logical + (w.prefill_kv_bytes() if has_prefill else 0)
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_ms = kern_ms["decode"]
+    achieved = kv_unique / (dec_ms * 1e-3) / 1e9
+
+    # achievable copy bandwidth, same process (context for the peak)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.cache_dtype if w.cache_dtype != "fp8" else "fp8-e4m3 KV, bf16 Q",
+        "data": "synthetic (seeded; no dataset, no weights)",
+        "config": {
+            "workload": w.name, "seed": w.seed, "batch": w.batch, "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "context_tokens": int(w.context_lens.sum()), "new_tokens": int(len(w.new_slots)),
+            "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
+            "pool_blocks": w.num_blocks, "layer_copies": R,
+        },
+        "us_per_layer_step": round(ms_per_step * 1e3, 3),
+        "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),
+        "kv_bytes_logical": kv_logical,
+        "kv_bytes_unique": kv_unique,
+        "kernels_us": {k: round(v * 1e3, 3) for k, v in kern_ms.items()},
+        "copy_GBps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    if has_prefill:
+        pf_ms = kern_ms["prefill_chunk"]
+        result["prefill_tflops"] = round(w.prefill_flops() / (pf_ms * 1e-3) / 1e12, 2)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, ms_per_step)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s, gpu_ms):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's
+    decode sequences; scaled to the metric's unit (KV GB/s)."""
+    from oracle import paged_attention as opa
+    import torch
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def raw(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.batch)
+    st = opa.STORAGE_DTYPES[w.cache_dtype]
+    kp = np.zeros((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim), st)
+    vp = np.zeros((w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size), st)
+    qh = raw(w.q)
+    done, tokens, elapsed = [], 0, 0.0
+    for b in order:
+        n = -(-int(w.context_lens[b]) // w.block_size)
+        blocks = w.block_tables[b, :n].astype(np.int64)
+        sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
+        idx = torch.as_tensor(sel, device=w.fill_k.device)
+        kp, vp = opa.oracle_append(kp, vp, raw(w.fill_k[idx]), raw(w.fill_v[idx]),
+                                   w.fill_slots[sel], w.in_dtype, w.cache_dtype, w.k_scale,
+                                   w.v_scale, w.block_size)
+        t = time.perf_counter()
+        opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables, w.context_lens,
+                          w.scale, w.k_scale, w.v_scale, w.block_size, seqs=[int(b)])
+        elapsed += time.perf_counter() - t
+        done.append(int(b))
+        tokens += int(w.context_lens[b])
+        if elapsed >= budget_s:
+            break
+    kv = tokens * w.kv_bytes_per_token()
+    return {
+        "value": round(kv / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "fp64 oracle decode of %d of %d sequences (%d context tokens, %.1f s), "
+                  "host affinity %d cores" % (len(done), w.batch, tokens, elapsed,
+                                              len(os.sched_getaffinity(0))),
+        "seconds": round(elapsed, 3),
+        "gpu_over_cpu": round((w.decode_kv_bytes_logical() / (gpu_ms * 1e-3)) / (kv / elapsed), 1)
+        if elapsed > 0 else None,
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * pa.h -- C ABI of libpagedattn: attention over a paged KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations are the ones the four pages on paged KV caches build their
+ * engines around (InferX, infer-lab, llm-infer, RustInfer):
+ *
+ *   pa_kv_append             write this step's new K/V rows into their pool
+ *                            slots (llm-infer, "What It Does": the per-layer
+ *                            graph holds "KV writes" and attention; InferX,
+ *                            "The kernels underneath": fp8 e4m3 KV writes
+ *                            with per-layer scales frozen at warm-up).
+ *   pa_decode                grouped-query softmax(scale * q K^T) V for one
+ *                            query token per sequence, K/V gathered through
+ *                            per-sequence block tables (infer-lab, technique
+ *                            table: "PagedAttention -- block allocator, block
+ *                            tables, refcounting"; llm-infer, "What It Does":
+ *                            "Paged KV cache with block tables").  Blocks
+ *                            may be shared by several sequences (infer-lab,
+ *                            RadixAttention row; llm-infer, prefix caching).
+ *                            With partition_size > 0 it computes split-K
+ *                            partials instead (flash-decoding).
+ *   pa_decode_splitk_reduce  merge those partials into the output.
+ *   pa_prefill_chunk         causal attention of prefill chunks over their
+ *                            cached prefix (InferX, "Status": chunked
+ *                            prefill; infer-lab, "chunked prefill ==
+ *                            one-shot prefill"; llm-infer, "ragged batched
+ *                            prefill").
+ *
+ * Conventions (the pages leave these open; the library fixes them):
+ *
+ *   block size   bs = 16 tokens.  Slot s = block * bs + offset.
+ *   K pool       [num_blocks][num_kv_heads][bs][head_dim]
+ *   V pool       [num_blocks][num_kv_heads][head_dim][bs]   (token-minor)
+ *   Q, out       [tokens][num_heads][head_dim], token-major, contiguous
+ *   GQA          query head hq reads KV head hq / G, G = num_heads / num_kv_heads
+ *   context_lens include the token appended in this step; a decode query
+ *                sits at position L - 1 and attends to positions 0 .. L-1.
+ *   block_tables [rows][max_blocks_per_seq] int32; only the first
+ *                ceil(L / bs) entries of a row are read.
+ *   fp8          OCP E4M3 ("e4m3fn", max 448, no inf).  One fp32 scale per KV
+ *                head, separate for K and V: real value = code * scale[h].
+ *                Encoding divides by the scale in IEEE binary32, rounds to
+ *                nearest even, saturates to +-448, keeps the sign of zero and
+ *                maps NaN to 0x7F.
+ *   L == 0       the output row is all zeros.
+ *
+ * Supported (q dtype, cache dtype): (F32, F32), (BF16, BF16), (BF16, FP8).
+ * head_dim in {64, 128}; block_size == 16; num_heads % num_kv_heads == 0 and
+ * 1 <= G <= 16.  Anything else returns PA_ERR_UNSUPPORTED without launching;
+ * there is no fallback path.
+ *
+ * Ownership and errors.  Every pointer is device memory owned by the caller;
+ * the library allocates nothing, frees nothing and keeps no state between
+ * calls.  Each call validates its host scalars and pointers (NULL, negative
+ * or inconsistent sizes -> PA_ERR_ARG), enqueues its kernels on `stream` and
+ * returns; launch failures surface as PA_ERR_LAUNCH.  Device-side contents
+ * are trusted, not checked: block ids must be < num_blocks, context lengths
+ * must fit the block table row, slots in one append must be distinct and
+ * < num_blocks * bs.  Calls on one stream run in order (append before the
+ * attention that reads the new token).
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_DT_F32 = 0,
+    PA_DT_BF16 = 1,
+    PA_DT_FP8_E4M3 = 2
+} pa_dtype_t;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_ARG = 1,          /* NULL pointer, negative or inconsistent size */
+    PA_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / block_size / G not built */
+    PA_ERR_LAUNCH = 3        /* the HIP runtime refused a launch */
+} pa_status_t;
+
+/*
+ * Write num_tokens new K/V rows into the pools.
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of in_dtype
+ *   slot_mapping   [num_tokens] int32; slot < 0 skips the token
+ *   k_scale/v_scale  [num_kv_heads] fp32, required iff cache_dtype == FP8
+ * (F32 -> F32) and (BF16 -> BF16) copy bytes; (BF16 -> FP8) encodes.
+ * Exactly the addressed elements change.  num_tokens == 0 is a no-op.
+ */
+pa_status_t pa_kv_append(const void* k_new, const void* v_new, pa_dtype_t in_dtype,
+                         void* k_cache, void* v_cache, pa_dtype_t cache_dtype,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* slot_mapping, int32_t num_tokens,
+                         int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, hipStream_t stream);
+
+/*
+ * Decode attention, one query token per sequence.
+ *   out            [batch][num_heads][head_dim], dtype = q_dtype (unused and
+ *                  may be NULL when partition_size > 0)
+ *   q              [batch][num_heads][head_dim]
+ *   block_tables   [batch][max_blocks_per_seq]; context_lens [batch]
+ *   scale          multiplies q . k (e.g. 1/sqrt(head_dim) rounded to fp32)
+ *   partition_size 0: one pass per (sequence, KV head) writes `out`.
+ *                  > 0 (a multiple of 16): split-K; partition p covers
+ *                  positions [p*PS, min(L, (p+1)*PS)) and writes, for every
+ *                  query head, m_p = max of scale*q.k (natural units),
+ *                  l_p = sum exp(s - m_p) and o_p = sum exp(s - m_p) v / l_p
+ *                  into part_max/part_sum [batch][num_heads][max_partitions]
+ *                  and part_out [batch][num_heads][max_partitions][head_dim]
+ *                  (fp32).  Partitions at or past ceil(L / PS) are not written.
+ *   max_partitions >= ceil(max_b L_b / PS) (host-known bound; sizes the grid)
+ */
+pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
+                      const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale,
+                      int32_t partition_size, int32_t max_partitions,
+                      float* part_max, float* part_sum, float* part_out,
+                      hipStream_t stream);
+
+/*
+ * Merge split-K partials (the layout pa_decode writes) into out
+ * [batch][num_heads][head_dim] of out_dtype (F32 or BF16):
+ *   M = max_p m_p,  w_p = l_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p
+ * over p < ceil(L_b / partition_size); L_b == 0 writes zeros.
+ * Supports max_partitions <= 4096.
+ */
+pa_status_t pa_decode_splitk_reduce(void* out, pa_dtype_t out_dtype,
+                                    const float* part_max, const float* part_sum,
+                                    const float* part_out, const int32_t* context_lens,
+                                    int32_t batch, int32_t num_heads, int32_t head_dim,
+                                    int32_t partition_size, int32_t max_partitions,
+                                    hipStream_t stream);
+
+/*
+ * Causal attention of prefill chunks over the paged cache (their own K/V
+ * already appended).  Chunk c owns query rows query_start_loc[c] ..
+ * query_start_loc[c+1]-1 (C_c rows, C_c <= max_query_len) and has context
+ * length context_lens[c] = P_c + C_c; its row i (position P_c + i) attends
+ * to positions 0 .. P_c + i.
+ *   out, q         [query_start_loc[num_chunks]][num_heads][head_dim]
+ *   block_tables   [num_chunks][max_blocks_per_seq]
+ */
+pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_dtype,
+                             const int32_t* query_start_loc, int32_t num_chunks,
+                             int32_t max_query_len,
+                             const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, hipStream_t stream);
+
+/* Static, never NULL. */
+const char* pa_status_string(pa_status_t status);
+
+/* Bytes of part_max + part_sum + part_out for a split-K decode (fp32). */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_partitions);
+
+/* Runs a one-wave kernel on the current device and checks its result:
+ * PA_ERR_LAUNCH when no gfx950 code object loads (a build for the wrong
+ * target must fail loudly, never silently). */
+pa_status_t pa_selftest(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

@@ -1,0 +1,106 @@
+// Device-side building blocks for the paged-attention kernels (gfx950 only).
+//
+// Everything here is CDNA4-specific: 64-lane wavefronts, the gfx950 MFMA
+// shapes v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32, the OCP fp8
+// conversion instructions and 16-byte global loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;                 // tokens per KV block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum CacheKind { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---- MFMA wrappers ---------------------------------------------------------
+// 16x16x32 bf16: lane l supplies A[row l%16][k 8*(l/16) .. +7] and
+// B[k 8*(l/16) .. +7][col l%16]; C/D lane l holds rows 4*(l/16)+i, col l%16.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x4 fp32: lane l supplies A[row l%16][k l/16] and B[k l/16][col l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- conversions -----------------------------------------------------------
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 OCP e4m3 codes (two dwords) -> 8 bf16 (exact: every e4m3 value is a bf16).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- cross-lane reductions over the four 16-lane groups --------------------
+__device__ __forceinline__ float max_over_groups(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- 16-byte global loads (non-temporal for streamed KV) --------------------
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16_cached(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---- workgroup -> work-item mapping that keeps neighbours on one XCD --------
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber them so that consecutive work items (e.g. the sequences of a
+// prefix-sharing group, which read the same blocks) run on the same XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    const int per = nblocks / kXcd;          // full rounds
+    const int rem = nblocks % kXcd;
+    const int xcd = bid % kXcd;
+    const int slot = bid / kXcd;
+    if (slot >= per) return bid;             // tail of an incomplete round
+    (void)rem;
+    return xcd * per + slot;
+}
+
+}  // namespace pa

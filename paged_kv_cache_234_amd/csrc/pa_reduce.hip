@@ -1,0 +1,133 @@
+// Split-K (flash-decoding) reduce: merge per-partition softmax statistics.
+//
+// For each (sequence b, query head hq) with P = ceil(L_b / PS) partitions:
+//   M = max_p m_p,  w_p = l_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
+// This is the standard merge of online-softmax partial states (the same
+// identity that makes tiled attention equal to naive attention, infer-lab's
+// invariant list); the pages themselves do not describe split-K.
+//
+// One 256-thread workgroup per (b, hq): the weights go to LDS, then each
+// thread accumulates float4 columns of o_p over a strided subset of the
+// partitions and the subsets are summed through LDS.
+#include "pa_internal.hpp"
+
+namespace pa {
+
+constexpr int kMaxReducePartitions = 4096;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void reduce_kernel(void* __restrict__ out,
+                                                     const float* __restrict__ part_max,
+                                                     const float* __restrict__ part_sum,
+                                                     const float* __restrict__ part_out,
+                                                     const int32_t* __restrict__ context_lens,
+                                                     int num_heads, int partition_size,
+                                                     int max_partitions) {
+    constexpr int NT = 256, D4 = D / 4, NPH = NT / D4;
+    __shared__ float s_w[kMaxReducePartitions];
+    __shared__ float s_red[NT / kWave];
+    __shared__ f32x4 s_acc[NPH][D4];
+
+    const int bh = blockIdx.x;
+    const int b = bh / num_heads;
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const int L = context_lens[b];
+    // never trust L beyond the caller-declared bound: it sizes LDS and rows
+    const int P = min((L + partition_size - 1) / partition_size, max_partitions);
+    const long base = (long)bh * max_partitions;
+
+    float M = -INFINITY;
+    for (int i = tid; i < P; i += NT) M = fmaxf(M, part_max[base + i]);
+    M = wave_max(M);
+    if ((tid & (kWave - 1)) == 0) s_red[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+
+    float wsum = 0.f;
+    for (int i = tid; i < P; i += NT) {
+        const float w = part_sum[base + i] * fast_exp2((part_max[base + i] - M) * kLog2e);
+        s_w[i] = w;
+        wsum += w;
+    }
+    wsum = wave_sum(wsum);
+    if ((tid & (kWave - 1)) == 0) s_red[wave] = wsum;
+    __syncthreads();
+    const float W = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+
+    const int d4 = tid % D4, ph = tid / D4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f32x4* po = reinterpret_cast<const f32x4*>(part_out + base * D) + d4;
+    for (int i = ph; i < P; i += NPH) acc += s_w[i] * po[(long)i * D4];
+    s_acc[ph][d4] = acc;
+    __syncthreads();
+    if (tid < D4) {
+        f32x4 s = s_acc[0][tid];
+#pragma unroll
+        for (int k = 1; k < NPH; ++k) s += s_acc[k][tid];
+        const float inv = (P > 0) ? 1.0f / W : 0.0f;
+        s = (P > 0) ? s * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (OUT_BF16) {
+            uint16_t* o = static_cast<uint16_t*>(out) + (long)bh * D + 4 * tid;
+            u32x2 pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+            *reinterpret_cast<u32x2*>(o) = pk;
+        } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (long)bh * D + 4 * tid) = s;
+        }
+    }
+}
+
+template <int D, bool OUT_BF16>
+static hipError_t launch_reduce(void* out, const float* pm, const float* ps, const float* po,
+                                const int32_t* lens, int batch, int num_heads, int partition_size,
+                                int max_partitions, hipStream_t stream) {
+    const long grid = (long)batch * num_heads;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((reduce_kernel<D, OUT_BF16>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       out, pm, ps, po, lens, num_heads, partition_size, max_partitions);
+    return hipGetLastError();
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status_t pa_decode_splitk_reduce(void* out, pa_dtype_t out_dtype,
+                                               const float* part_max, const float* part_sum,
+                                               const float* part_out, const int32_t* context_lens,
+                                               int32_t batch, int32_t num_heads, int32_t head_dim,
+                                               int32_t partition_size, int32_t max_partitions,
+                                               hipStream_t stream) {
+    if (!valid_dtype(out_dtype)) return PA_ERR_ARG;
+    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || partition_size <= 0 || max_partitions < 1)
+        return PA_ERR_ARG;
+    if (out_dtype == PA_DT_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (max_partitions > kMaxReducePartitions) return PA_ERR_UNSUPPORTED;
+    if (batch == 0) return PA_OK;
+    if (!out || !part_max || !part_sum || !part_out || !context_lens) return PA_ERR_ARG;
+    hipError_t e;
+    const bool bf = out_dtype == PA_DT_BF16;
+    if (head_dim == 128)
+        e = bf ? launch_reduce<128, true>(out, part_max, part_sum, part_out, context_lens, batch,
+                                          num_heads, partition_size, max_partitions, stream)
+               : launch_reduce<128, false>(out, part_max, part_sum, part_out, context_lens, batch,
+                                           num_heads, partition_size, max_partitions, stream);
+    else
+        e = bf ? launch_reduce<64, true>(out, part_max, part_sum, part_out, context_lens, batch,
+                                         num_heads, partition_size, max_partitions, stream)
+               : launch_reduce<64, false>(out, part_max, part_sum, part_out, context_lens, batch,
+                                          num_heads, partition_size, max_partitions, stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}

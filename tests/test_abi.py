@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/pa.h declares, and rejects bad host arguments before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_234_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pa_[a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(4):
+        assert _lib.status_string(s).startswith("PA_")
+    assert _lib.status_string(99) == "PA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    assert _lib.pa_decode_workspace_bytes(8, 32, 128, 256) == 8 * 32 * 256 * 4 * 130
+    assert _lib.pa_decode_workspace_bytes(-1, 32, 128, 256) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(out=None, q=None, q_dt=1, k=None, v=None, c_dt=1, ks=None, vs=None, bt=None, W=4,
+             lens=None, B=2, hq=8, hkv=2, d=128, bs=16, scale=0.1, ps=0, pmax=1)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["q_dt"], a["k"], a["v"], a["c_dt"], a["ks"], a["vs"],
+                         a["bt"], a["W"], a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"],
+                         a["scale"], a["ps"], a["pmax"], None, None, None, None)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), _lib.PA_ERR_ARG),                                    # null pointers
+    (dict(hq=7, hkv=2), _lib.PA_ERR_ARG),                         # Hq not a multiple of Hkv
+    (dict(d=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(bs=32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(hq=34, hkv=2), _lib.PA_ERR_UNSUPPORTED),                # G = 17
+    (dict(q_dt=0, c_dt=1), _lib.PA_ERR_UNSUPPORTED),              # f32 q over bf16 cache
+    (dict(q_dt=1, c_dt=2), _lib.PA_ERR_ARG),                      # fp8 without scales
+    (dict(q_dt=5), _lib.PA_ERR_ARG),
+    (dict(B=-1), _lib.PA_ERR_ARG),
+    (dict(B=0), _lib.PA_OK),                                      # empty batch: nothing to do
+])
+def test_decode_argument_validation(kw, status):
+    lib = _lib.load()
+    assert _decode(lib, **kw) == status
+
+
+def test_decode_rejects_bad_partitioning():
+    lib = _lib.load()
+    common = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE)
+    assert _decode(lib, ps=24, pmax=4, **common) == _lib.PA_ERR_ARG       # not a multiple of 16
+    assert _decode(lib, ps=32, pmax=4, **common) == _lib.PA_ERR_ARG       # no partial buffers
+    assert _decode(lib, ps=-16, **common) == _lib.PA_ERR_ARG
+    assert _decode(lib, scale=float("nan"), **common) == _lib.PA_ERR_ARG
+
+
+def test_append_reduce_prefill_validation():
+    lib = _lib.load()
+    # append: fp8 cache needs scales; zero tokens is a no-op
+    assert lib.pa_kv_append(FAKE, FAKE, 1, FAKE, FAKE, 2, None, None, FAKE, 4, 8, 2, 128, 16,
+                            None) == _lib.PA_ERR_ARG
+    assert lib.pa_kv_append(None, None, 1, None, None, 1, None, None, None, 0, 8, 2, 128, 16,
+                            None) == _lib.PA_OK
+    assert lib.pa_kv_append(FAKE, FAKE, 0, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16,
+                            None) == _lib.PA_ERR_UNSUPPORTED
+    # reduce: too many partitions for the LDS weight table
+    assert lib.pa_decode_splitk_reduce(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 512, 5000,
+                                       None) == _lib.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_splitk_reduce(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 0, 4,
+                                       None) == _lib.PA_ERR_ARG
+    # prefill: nothing to do for zero chunks; null pointers rejected otherwise
+    assert lib.pa_prefill_chunk(None, None, 1, None, 0, 0, None, None, 1, None, None, None, 4,
+                                None, 8, 2, 128, 16, 0.1, None) == _lib.PA_OK
+    assert lib.pa_prefill_chunk(None, None, 1, None, 2, 64, None, None, 1, None, None, None, 4,
+                                None, 8, 2, 128, 16, 0.1, None) == _lib.PA_ERR_ARG
