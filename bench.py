@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the kernels one by one instead of replaying captured graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU budget of the oracle baseline")
@@ -65,7 +67,7 @@ def main():
     torch.cuda.set_device(0)
     pa_selftest()
     w = make_config(args.config, seed=args.seed, device=dev)
-    ps = args.partition_size or DEFAULT_PS[args.config]
+    ps = DEFAULT_PS[args.config] if args.partition_size is None else args.partition_size
 
     def i32(a):
         return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
@@ -107,12 +109,16 @@ def main():
         pool.append(new_k, new_v, new_slots)
         if ev is not None:
             ev[1].record(stream)
-        pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
-                  partition_size=ps, max_partitions=pmax, part_max=part_max, part_sum=part_sum,
-                  part_out=part_out)
+        if ps > 0:
+            pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
+                      partition_size=ps, max_partitions=pmax, part_max=part_max,
+                      part_sum=part_sum, part_out=part_out)
+        else:
+            pa_decode(out, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale)
         if ev is not None:
             ev[2].record(stream)
-        pa_decode_splitk_reduce(out, part_max, part_sum, part_out, lens, ps)
+        if ps > 0:
+            pa_decode_splitk_reduce(out, part_max, part_sum, part_out, lens, ps)
         if ev is not None:
             ev[3].record(stream)
         if has_prefill:
@@ -121,8 +127,43 @@ def main():
             if ev is not None:
                 ev[4].record(stream)
 
-    for i in range(args.warmup):
+    def decode_only(layer):
+        pool = pools[layer % R]
+        if ps > 0:
+            pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
+                      partition_size=ps, max_partitions=pmax, part_max=part_max,
+                      part_sum=part_sum, part_out=part_out)
+        else:
+            pa_decode(out, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale)
+
+    for i in range(max(args.warmup, 1)):
         step(i)
+        decode_only(i)
+    torch.cuda.synchronize()
+
+    # The engines on the pages replay their decode step as a captured graph
+    # covering every layer; here one graph holds the K timed layer-steps (each
+    # on the next layer copy), another the warm-up steps, a third the K
+    # decode kernels alone.
+    def steps_of(fn, first, count):
+        for i in range(count):
+            fn(first + i)
+
+    def captured(fn, first, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            steps_of(fn, first, count)
+        return g
+
+    if not args.eager:
+        g_warm = captured(step, 0, max(args.warmup, 1))
+        g_steps = captured(step, args.warmup, args.steps)
+        g_decode = captured(decode_only, args.warmup, args.steps)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        g_warm.replay()
+    else:
+        steps_of(step, 0, args.warmup)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ------------------------------------
@@ -130,13 +171,27 @@ def main():
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    if args.eager:
+        steps_of(step, args.warmup, args.steps)
+    else:
+        g_steps.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-kernel durations (HIP events on the launch stream) -------------
+    # ---- the decode kernel alone: K back-to-back launches between two events
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    if args.eager:
+        steps_of(decode_only, args.warmup, args.steps)
+    else:
+        g_decode.replay()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = d0.elapsed_time(d1) / args.steps
+
+    # ---- per-kernel durations, eager, HIP events around each launch ---------
     nev = 5 if has_prefill else 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -151,8 +206,7 @@ def main():
     kv_unique = w.decode_kv_bytes_unique()
     step_bytes = kv_logical + (w.prefill_kv_bytes() if has_prefill else 0)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_ms = kern_ms["decode"]
-    achieved = kv_unique / (dec_ms * 1e-3) / 1e9
+    achieved = kv_unique / (decode_ms * 1e-3) / 1e9
 
     # achievable copy bandwidth, same process (context for the peak)
     nbytes = 1 << 30
@@ -192,11 +246,14 @@ def main():
         "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),
         "kv_bytes_logical": kv_logical,
         "kv_bytes_unique": kv_unique,
-        "kernels_us": {k: round(v * 1e3, 3) for k, v in kern_ms.items()},
+        "launch": "eager" if args.eager else "one HIP graph holding the K layer-steps",
+        "decode_kernel_us": round(decode_ms * 1e3, 3),
+        "eager_event_us": {k: round(v * 1e3, 3) for k, v in kern_ms.items()},
         "copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "decode",
+            "duration_us": round(decode_ms * 1e3, 3),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -231,8 +288,10 @@ def cpu_baseline(w, budget_s, gpu_ms):
     rng = np.random.default_rng(0)
     order = rng.permutation(w.batch)
     st = opa.STORAGE_DTYPES[w.cache_dtype]
-    kp = np.zeros((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim), st)
-    vp = np.zeros((w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size), st)
+    shape_k, shape_v = opa.pool_shapes(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
+                                       w.block_size)
+    kp = np.zeros(shape_k, st)
+    vp = np.zeros(shape_v, st)
     qh = raw(w.q)
     done, tokens, elapsed = [], 0, 0.0
     for b in order:

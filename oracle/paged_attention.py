@@ -24,7 +24,9 @@ Sources (the four pages on paged KV caches):
 Storage conventions (the pages leave them open; these are the readings the
 library also uses, so appended bytes can be compared one for one):
 
-* K pool: [num_blocks][num_kv_heads][block_size][head_dim]
+* K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X] with
+  X = 16 bytes of elements (4 fp32, 8 bf16, 16 fp8): for each run of X
+  consecutive head-dim elements, the block's 16 tokens one after another.
 * V pool: [num_blocks][num_kv_heads][head_dim][block_size]  (token-minor)
 * element storage: "f32" -> float32, "bf16" -> uint16 bit patterns,
   "fp8" -> uint8 OCP E4M3 codes with one fp32 scale per KV head (K and V
@@ -46,6 +48,18 @@ from . import bf16 as _bf16
 from . import fp8_e4m3 as _fp8
 
 STORAGE_DTYPES = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+
+
+def k_chunk(dtype):
+    """X: head-dim elements per 16-byte run of the K pool layout."""
+    return 16 // np.dtype(STORAGE_DTYPES[dtype]).itemsize
+
+
+def pool_shapes(num_blocks, num_kv_heads, head_dim, dtype, block_size=16):
+    """(K pool shape, V pool shape) of the storage layout."""
+    x = k_chunk(dtype)
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
 
 
 # ---------------------------------------------------------------------------
@@ -87,9 +101,9 @@ def oracle_append(k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype, cache_dt
     """Return copies of the pools after writing the new tokens' K/V.
 
     For every token t with slot_mapping[t] >= 0: block = slot // block_size,
-    offset = slot % block_size, and for every KV head h
-        K[block, h, offset, :] = enc(k_new[t, h, :]),
-        V[block, h, :, offset] = enc(v_new[t, h, :]).
+    offset = slot % block_size, and for every KV head h and head-dim index d
+        K[block, h, d // X, offset, d % X] = enc(k_new[t, h, d]),
+        V[block, h, d, offset]             = enc(v_new[t, h, d]).
     Tokens with a negative slot are skipped.  No other element changes.
     Duplicate slots are a caller error (result unspecified) and are rejected.
     """
@@ -109,8 +123,10 @@ def oracle_append(k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype, cache_dt
     off = s % block_size
     k_enc = encode_for_cache(np.asarray(k_new)[keep], in_dtype, cache_dtype, k_scale)
     v_enc = encode_for_cache(np.asarray(v_new)[keep], in_dtype, cache_dtype, v_scale)
-    k_out[blk, :, off, :] = k_enc          # [T, Hkv, D] lands on (blk, :, off, :)
-    v_out[blk, :, :, off] = v_enc          # [T, Hkv, D] lands on (blk, :, :, off)
+    t_n, hkv, d = k_enc.shape
+    x = k_pool.shape[4]
+    k_out[blk, :, :, off, :] = k_enc.reshape(t_n, hkv, d // x, x)   # lands on (blk, :, :, off, :)
+    v_out[blk, :, :, off] = v_enc                                   # lands on (blk, :, :, off)
     return k_out, v_out
 
 
@@ -128,17 +144,17 @@ def gather_sequence(k_pool, v_pool, block_table_row, context_len, cache_dtype,
     """
     L = int(context_len)
     num_blocks, hkv = k_pool.shape[0], k_pool.shape[1]
-    d = k_pool.shape[3]
+    d = k_pool.shape[2] * k_pool.shape[4]
     n = -(-L // block_size)
     ids = np.asarray(block_table_row[:n], dtype=np.int64)
     if len(ids) != n or (n and (ids.min() < 0 or ids.max() >= num_blocks)):
         raise ValueError("block table does not cover the context with valid ids")
-    kb = storage_to_f64(k_pool[ids], cache_dtype)                 # [n, Hkv, bs, D]
+    kb = storage_to_f64(k_pool[ids], cache_dtype)                 # [n, Hkv, D/X, bs, X]
     vb = storage_to_f64(v_pool[ids], cache_dtype)                 # [n, Hkv, D, bs]
     if cache_dtype == "fp8":
-        kb = kb * np.asarray(k_scale, dtype=np.float32).astype(np.float64)[None, :, None, None]
+        kb = kb * np.asarray(k_scale, dtype=np.float32).astype(np.float64)[None, :, None, None, None]
         vb = vb * np.asarray(v_scale, dtype=np.float32).astype(np.float64)[None, :, None, None]
-    K = kb.transpose(0, 2, 1, 3).reshape(n * block_size, hkv, d)[:L]
+    K = kb.transpose(0, 3, 1, 2, 4).reshape(n * block_size, hkv, d)[:L]
     V = vb.transpose(0, 3, 1, 2).reshape(n * block_size, hkv, d)[:L]
     return K, V
 

@@ -102,7 +102,13 @@ def _stream(stream):
 
 
 def _pool_dims(k_cache, v_cache):
-    nb, hkv, bs, d = k_cache.shape
+    """K [NB, Hkv, D/X, bs, X] (X = 16 bytes of elements), V [NB, Hkv, D, bs]."""
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_dim/X, block_size, X]")
+    nb, hkv, dx, bs, x = k_cache.shape
+    if x * k_cache.element_size() != 16:
+        raise ValueError("k_cache's last dimension must hold 16 bytes")
+    d = dx * x
     if tuple(v_cache.shape) != (nb, hkv, d, bs) or v_cache.dtype != k_cache.dtype:
         raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size] "
                          "of k_cache's dtype")

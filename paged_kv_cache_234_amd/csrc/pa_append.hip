@@ -6,9 +6,9 @@
 // at warm-up.  Here the scale is one fp32 value per KV head (K and V apart).
 //
 // One thread moves 8 consecutive head_dim elements of one (token, head):
-// a 16-byte (bf16) or 32-byte (fp32) read, the same-sized contiguous store
-// into the K row, and 8 element stores into the token-minor V tile
-// (V[block][head][d][offset]).  fp8 encoding is an IEEE binary32 divide by
+// a 16-byte (bf16) or 32-byte (fp32) read, contiguous stores into the K pool
+// (K[block][head][d / X][offset][d % X], X = 16 bytes of elements) and 8
+// element stores into the token-minor V tile (V[block][head][d][offset]).  fp8 encoding is an IEEE binary32 divide by
 // the scale, saturation to +-448 and the hardware's round-to-nearest-even
 // OCP e4m3 conversion; NaN is written as 0x7F.
 #include "pa_internal.hpp"
@@ -48,7 +48,11 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
     const long blk = slot / kBlock;
     const int off = slot % kBlock;
     const long src = (t * num_kv_heads + h) * D + 8 * c;
-    const long kdst = ((blk * num_kv_heads + h) * kBlock + off) * D + 8 * c;
+    // element index of K[blk][h][d / X][off][d % X] for d = 8c (X elements per 16 bytes)
+    constexpr int X = (CACHE == kF32) ? 4 : (CACHE == kBF16 ? 8 : 16);
+    auto kidx = [&](int d) -> long {
+        return (((blk * num_kv_heads + h) * (D / X) + d / X) * kBlock + off) * X + d % X;
+    };
     const long vdst = ((blk * num_kv_heads + h) * D + 8 * c) * kBlock + off;
 
     if (CACHE == kF32) {
@@ -56,9 +60,9 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
         const float* vsrc = static_cast<const float*>(v_new) + src;
         u32x4 k0 = load16_cached(ks), k1 = load16_cached(ks + 4);
         u32x4 v0 = load16_cached(vsrc), v1 = load16_cached(vsrc + 4);
-        float* kd = reinterpret_cast<float*>(k_cache) + kdst;
-        *reinterpret_cast<u32x4*>(kd) = k0;
-        *reinterpret_cast<u32x4*>(kd + 4) = k1;
+        float* kc = reinterpret_cast<float*>(k_cache);
+        *reinterpret_cast<u32x4*>(kc + kidx(8 * c)) = k0;
+        *reinterpret_cast<u32x4*>(kc + kidx(8 * c + 4)) = k1;
         uint32_t* vd = reinterpret_cast<uint32_t*>(v_cache) + vdst;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
     } else if (CACHE == kBF16) {
         u32x4 kv = load16_cached(static_cast<const uint16_t*>(k_new) + src);
         u32x4 vv = load16_cached(static_cast<const uint16_t*>(v_new) + src);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kdst) = kv;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kidx(8 * c)) = kv;
         uint16_t* vd = reinterpret_cast<uint16_t*>(v_cache) + vdst;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
             vq[w] = vlo | (vhi << 16);
         }
         u32x2 kk = {kq[0], kq[1]};
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(k_cache) + kdst) = kk;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(k_cache) + kidx(8 * c)) = kk;
         uint8_t* vd = reinterpret_cast<uint8_t*>(v_cache) + vdst;
 #pragma unroll
         for (int e = 0; e < 8; ++e) vd[e * kBlock] = (uint8_t)(vq[e >> 2] >> (8 * (e & 3)));

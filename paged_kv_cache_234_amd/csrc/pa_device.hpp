@@ -67,15 +67,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---- cross-lane reductions over the four 16-lane groups --------------------
+// gfx950's v_permlane32_swap / v_permlane16_swap exchange 32- and 16-lane
+// halves between two VGPRs without going through LDS: starting from two
+// copies of x, lane l ends up holding x[l] and x[l^32] (x[l^16]) across the
+// two registers, so max/sum over lanes {l, l^16, l^32, l^48} is four VALU ops.
+// The swaps are issued through inline asm on two distinct register operands:
+// the compiler's builtin folds a swap of two equal inputs to two equal
+// outputs, which drops the exchange.  The s_nop covers the VALU-write ->
+// permlane-read hazard.
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float max_over_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    permlane32_swap(a, b);
+    uint32_t c = __builtin_bit_cast(uint32_t,
+                                    fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    uint32_t d = c;
+    permlane16_swap(c, d);
+    return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    permlane32_swap(a, b);
+    uint32_t c = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    uint32_t d = c;
+    permlane16_swap(c, d);
+    return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -89,18 +110,17 @@ __device__ __forceinline__ u32x4 load16_cached(const void* p) {
 }
 
 // ---- workgroup -> work-item mapping that keeps neighbours on one XCD --------
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Renumber them so that consecutive work items (e.g. the sequences of a
-// prefix-sharing group, which read the same blocks) run on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Renumber them so that every run of 8 consecutive work items executes
+// on one XCD at about the same time, while successive runs rotate over the
+// XCDs: items that read the same KV blocks (the sequences of a
+// prefix-sharing group, laid out next to each other) share an L2, and the
+// work still spreads evenly over the chip at 8-item granularity.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    constexpr int kXcd = 8;
-    const int per = nblocks / kXcd;          // full rounds
-    const int rem = nblocks % kXcd;
-    const int xcd = bid % kXcd;
-    const int slot = bid / kXcd;
-    if (slot >= per) return bid;             // tail of an incomplete round
-    (void)rem;
-    return xcd * per + slot;
+    constexpr int kXcd = 8, kRun = 8, kRound = kXcd * kRun;
+    if (bid >= (nblocks / kRound) * kRound) return bid;     // incomplete last round
+    const int slot = bid / kXcd, xcd = bid % kXcd;
+    return kRound * (slot / kRun) + kRun * xcd + slot % kRun;
 }
 
 }  // namespace pa

@@ -41,12 +41,18 @@ struct PrefillArgs {
 template <int KIND> struct PQType { using T = uint16_t; };
 template <> struct PQType<kF32> { using T = float; };
 
-template <int KIND, int D, int NW>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+// Query tiles per wavefront: each K/V tile a wavefront loads (and, for fp8,
+// widens to bf16) feeds NC * 16 query rows.
+constexpr int prefill_tiles_per_wave(int kind, int d) {
+    return kind == kF32 ? 1 : 2;
+}
+
+template <int KIND, int D, int NW, int NC>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void prefill_kernel(PrefillArgs a) {
     using Ops = TileOps<KIND, D>;
     using QT = typename PQType<KIND>::T;
-    constexpr int TT = Ops::TT, TB = Ops::TB, NVT = Ops::NVT, ELEM = Ops::ELEM;
+    constexpr int TT = Ops::TT, NVT = Ops::NVT, ELEM = Ops::ELEM;
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -59,24 +65,31 @@ void prefill_kernel(PrefillArgs a) {
     const int C = a.query_start_loc[c + 1] - q0;
     const int L = a.context_lens[c];
     const int P = L - C;
-    const int row0 = (tg * NW + wave) * a.npos;          // first chunk row of this tile
+    const int npos = a.npos;
+    const int row0 = (tg * NW + wave) * NC * npos;       // first chunk row of this wavefront
     if (row0 >= C || P < 0) return;
-    const int rows = min(a.npos, C - row0);
+    const int wrows = min(NC * npos, C - row0);
 
     const int g = lane & 15, grp = lane >> 4;
-    const int pi = g / a.group, gh = g % a.group;        // column -> (row, head)
-    const bool col_valid = pi < rows;
-    const QT* qrow = reinterpret_cast<const QT*>(a.q) +
-                     ((long)(q0 + row0 + pi) * a.num_heads + h * a.group + gh) * D;
-    typename Ops::Q qop;
-    Ops::load_q(qop, qrow, col_valid, lane);
+    const int pi = g / a.group, gh = g % a.group;        // column -> (row in tile, head)
+    typename Ops::Q qop[NC];
+    int my_last[NC];                                     // last key each column sees
+    bool col_valid[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int r = n * npos + pi;
+        col_valid[n] = pi < npos && r < wrows;
+        const QT* qrow = reinterpret_cast<const QT*>(a.q) +
+                         ((long)(q0 + row0 + r) * a.num_heads + h * a.group + gh) * D;
+        Ops::load_q(qop[n], qrow, col_valid[n], lane);
+        my_last[n] = P + row0 + (col_valid[n] ? r : 0);
+    }
 
     float cs = a.scale_log2;
     if (KIND == kFP8) cs *= a.k_scale[h];
 
-    const int my_last = P + row0 + (col_valid ? pi : 0); // last key this column sees
-    const int min_last = P + row0;                       // smallest over the tile
-    const int kend = P + row0 + rows;                    // keys [0, kend) are touched
+    const int min_last = P + row0;                       // smallest over the wavefront
+    const int kend = P + row0 + wrows;                   // keys [0, kend) are touched
     const int ntiles = (kend + TT - 1) / TT;
     const int last_blk = (kend - 1) / kBlock;
     const int32_t* bt = a.block_tables + (long)c * a.max_blocks_per_seq;
@@ -85,56 +98,37 @@ void prefill_kernel(PrefillArgs a) {
     const long blk_stride = head_stride * a.num_kv_heads;
     const char* kbase = a.k_cache + h * head_stride;
     const char* vbase = a.v_cache + h * head_stride;
-    const int kb = Ops::k_block(lane), vb = Ops::v_block(lane);
-
-    auto issue = [&](typename Ops::Regs& r, int n) {
-        const int lb = n * TB;
-        int phys[TB];
-#pragma unroll
-        for (int j = 0; j < TB; ++j) phys[j] = bt[min(lb + j, last_blk)];
-        int pk = phys[0], pv = phys[0];
-#pragma unroll
-        for (int j = 1; j < TB; ++j) {
-            pk = (kb == j) ? phys[j] : pk;
-            pv = (vb == j) ? phys[j] : pv;
-        }
-        Ops::load(r, kbase + (long)pk * blk_stride, vbase + (long)pv * blk_stride, lane);
-    };
-
-    WaveSoftmax<KIND, D> st;
+    WaveSoftmax<KIND, D, NC> st;
     st.init();
-    auto compute = [&](typename Ops::Regs& r, int n) {
-        const int t0 = n * TT;
-        const int nvalid = kend - t0;
-        const bool masked = (t0 + TT - 1 > min_last) || (nvalid < TT);
-        st.step(r, qop, cs, nvalid, my_last - t0, masked, lane);
-    };
-
-    {
-        typename Ops::Regs ra, rb;
-        issue(ra, 0);
-        for (int n = 0; n < ntiles; n += 2) {
-            if (n + 1 < ntiles) issue(rb, n + 1);
-            compute(ra, n);
-            if (n + 1 >= ntiles) break;
-            if (n + 2 < ntiles) issue(ra, n + 2);
-            compute(rb, n + 1);
-        }
-    }
-
-    const float l = sum_over_groups(st.l);
-    if (!col_valid) return;
-    const float inv = (KIND == kFP8 ? a.v_scale[h] : 1.0f) / l;
-    const long orow = ((long)(q0 + row0 + pi) * a.num_heads + h * a.group + gh) * D;
+    stream_tiles<KIND, D>(bt, 0, last_blk, 0, ntiles, kbase, vbase, blk_stride, lane,
+                          [&](typename Ops::Regs& r, int n) {
+                              const int t0 = n * TT;
+                              const int nvalid = kend - t0;
+                              const bool masked = (t0 + TT - 1 > min_last) || (nvalid < TT);
+                              int limit[NC];
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) {
-        const int d = 16 * t + 4 * grp;
-        const f32x4 v = st.o[t] * inv;
-        if (KIND == kF32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d) = v;
-        } else {
-            u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + d) = pk;
+                              for (int k = 0; k < NC; ++k) limit[k] = my_last[k] - t0;
+                              st.step(r, qop, cs, nvalid, limit, masked, lane);
+                          });
+
+    const float vs = KIND == kFP8 ? a.v_scale[h] : 1.0f;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const float l = sum_over_groups(st.l[n]);        // against the reference mr
+        if (!col_valid[n]) continue;
+        const float inv = vs / l;
+        const long orow =
+            ((long)(q0 + row0 + n * npos + pi) * a.num_heads + h * a.group + gh) * D;
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int d = 16 * t + 4 * grp;
+            const f32x4 v = st.o[n][t] * inv;
+            if (KIND == kF32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d) = v;
+            } else {
+                u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + d) = pk;
+            }
         }
     }
 }
@@ -142,14 +136,15 @@ void prefill_kernel(PrefillArgs a) {
 template <int KIND, int D>
 static hipError_t launch_prefill(PrefillArgs a, int num_chunks, int max_query_len,
                                  hipStream_t stream) {
-    constexpr int NW = 4;
+    constexpr int NW = 4, NC = prefill_tiles_per_wave(KIND, D);
     const int tiles = (max_query_len + a.npos - 1) / a.npos;
-    a.wg_per_head = (tiles + NW - 1) / NW;
+    const int waves = (tiles + NC - 1) / NC;
+    a.wg_per_head = (waves + NW - 1) / NW;
     const long grid = (long)num_chunks * a.num_kv_heads * a.wg_per_head;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_kernel<KIND, D, NW>), dim3((unsigned)grid), dim3(NW * kWave), 0,
-                       stream, a);
+    hipLaunchKernelGGL((prefill_kernel<KIND, D, NW, NC>), dim3((unsigned)grid), dim3(NW * kWave),
+                       0, stream, a);
     return hipGetLastError();
 }
 

@@ -88,14 +88,79 @@ __global__ __launch_bounds__(256) void reduce_kernel(void* __restrict__ out,
     }
 }
 
+// Few partitions (max_partitions <= 64): one wavefront per (sequence, query
+// head), four per workgroup.  Lane p holds partition p's (m, l); the weights
+// are broadcast with v_readlane while each lane accumulates D/64 columns.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out,
+                                                          const float* __restrict__ part_max,
+                                                          const float* __restrict__ part_sum,
+                                                          const float* __restrict__ part_out,
+                                                          const int32_t* __restrict__ context_lens,
+                                                          int num_heads, int partition_size,
+                                                          int max_partitions, int npairs) {
+    constexpr int C = D / kWave;                       // columns per lane
+    const int lane = lane_id();
+    const int bh = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
+    if (bh >= npairs) return;
+    const int b = bh / num_heads;
+    const int L = context_lens[b];
+    const int P = min((L + partition_size - 1) / partition_size, max_partitions);
+    const long base = (long)bh * max_partitions;
+    const float mp = lane < P ? part_max[base + lane] : -INFINITY;
+    const float M = wave_max(mp);
+    const float w = lane < P ? part_sum[base + lane] * fast_exp2((mp - M) * kLog2e) : 0.f;
+    const float W = wave_sum(w);
+    float acc[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc[k] = 0.f;
+    const float* po = part_out + base * D + C * lane;
+    // eight partition rows in flight at a time
+    constexpr int U = 8;
+    for (int p0 = 0; p0 < P; p0 += U) {
+        float row[U][C];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < C; ++k)
+                row[u][k] = (p0 + u < P) ? po[(long)(p0 + u) * D + k] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int pp = min(p0 + u, kWave - 1);
+            const float wp = (p0 + u < P) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                           __builtin_bit_cast(int, w), pp))
+                                          : 0.f;
+#pragma unroll
+            for (int k = 0; k < C; ++k) acc[k] += wp * row[u][k];
+        }
+    }
+    const float inv = P > 0 ? 1.0f / W : 0.f;
+    if (OUT_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + (long)bh * D + C * lane;
+#pragma unroll
+        for (int k = 0; k < C; ++k) o[k] = f32_to_bf16_bits(acc[k] * inv);
+    } else {
+        float* o = static_cast<float*>(out) + (long)bh * D + C * lane;
+#pragma unroll
+        for (int k = 0; k < C; ++k) o[k] = acc[k] * inv;
+    }
+}
+
 template <int D, bool OUT_BF16>
 static hipError_t launch_reduce(void* out, const float* pm, const float* ps, const float* po,
                                 const int32_t* lens, int batch, int num_heads, int partition_size,
                                 int max_partitions, hipStream_t stream) {
-    const long grid = (long)batch * num_heads;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((reduce_kernel<D, OUT_BF16>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       out, pm, ps, po, lens, num_heads, partition_size, max_partitions);
+    const long pairs = (long)batch * num_heads;
+    if (pairs > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (max_partitions <= kWave) {
+        hipLaunchKernelGGL((reduce_wave_kernel<D, OUT_BF16>), dim3((unsigned)((pairs + 3) / 4)),
+                           dim3(256), 0, stream, out, pm, ps, po, lens, num_heads, partition_size,
+                           max_partitions, (int)pairs);
+    } else {
+        hipLaunchKernelGGL((reduce_kernel<D, OUT_BF16>), dim3((unsigned)pairs), dim3(256), 0,
+                           stream, out, pm, ps, po, lens, num_heads, partition_size,
+                           max_partitions);
+    }
     return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """Device memory for one layer's paged K/V pool (torch allocation only).
 
-K pool [num_blocks][num_kv_heads][16][head_dim], V pool
-[num_blocks][num_kv_heads][head_dim][16]; fp8 pools are uint8 OCP e4m3 codes
+K pool [num_blocks][num_kv_heads][head_dim / X][16][X] (X = 16 bytes of
+elements), V pool [num_blocks][num_kv_heads][head_dim][16]; fp8 pools are
+uint8 OCP e4m3 codes
 with per-KV-head fp32 scales.  The caller owns block assignment; this class
 only allocates and, optionally, fills every element with a NaN pattern so
 that a kernel reading a slot no sequence owns shows up as NaN.
@@ -22,7 +23,9 @@ class KVPool:
         self.cache_dtype = cache_dtype
         self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
         self.block_size = block_size
-        self.k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
+        x = 16 // torch.empty((), dtype=dt).element_size()
+        self.k = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dt,
+                             device=device)
         self.v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dt, device=device)
         if poison:
             self.poison()

@@ -36,8 +36,8 @@ def oracle_pool(w, seqs=None, chunks=None):
     """The oracle's own pool: poisoned, then oracle_append of the fill set
     (restricted to the slots of the given decode sequences / chunks)."""
     st = opa.STORAGE_DTYPES[w.cache_dtype]
-    shape_k = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-    shape_v = (w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size)
+    shape_k, shape_v = opa.pool_shapes(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
+                                       w.block_size)
     kp = np.full(shape_k, POISON[w.cache_dtype], dtype=st)
     vp = np.full(shape_v, POISON[w.cache_dtype], dtype=st)
     rows = np.arange(len(w.fill_slots))

@@ -1,0 +1,69 @@
+"""A captured layer-step (append + split-K decode + reduce + prefill chunk)
+replays to exactly the eager result, replay after replay, with eager work and
+synchronisations in between (the engines on the pages capture each decode
+step in a graph: InferX milestone M6, llm-infer "What It Does", RustInfer)."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_234_amd import (pa_decode, pa_decode_splitk_reduce, pa_kv_append,
+                                    pa_prefill_chunk)
+from tests.gpu_helpers import gpu_pool, i32
+from workloads import build_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_graph_replays_equal_eager(cache):
+    w = build_workload("g", seed=31, device="cuda", cache_dtype=cache, num_heads=16,
+                       num_kv_heads=4, head_dim=128, decode_lens=[1, 33, 700, 2000, 65],
+                       prefill_chunks=[(40, 70)])
+    pool = gpu_pool(w)
+    ps = 64
+    q = w.q.contiguous()
+    B, hq, d = q.shape
+    pmax = w.max_partitions(ps)
+    pm = torch.empty((B, hq, pmax), device="cuda")
+    psum = torch.empty_like(pm)
+    po = torch.empty((B, hq, pmax, d), device="cuda")
+    out = torch.empty_like(q)
+    qp = w.q_prefill.contiguous()
+    outp = torch.empty_like(qp)
+    lens, bt = i32(w.context_lens), i32(w.block_tables)
+    qsl, cbt, clens = i32(w.query_start_loc), i32(w.chunk_block_tables), i32(w.chunk_context_lens)
+    nk, nv, ns = w.new_k.contiguous(), w.new_v.contiguous(), i32(w.new_slots)
+
+    def step():
+        pa_kv_append(nk, nv, pool.k, pool.v, ns, pool.k_scale, pool.v_scale)
+        pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
+                  partition_size=ps, max_partitions=pmax, part_max=pm, part_sum=psum,
+                  part_out=po)
+        pa_decode_splitk_reduce(out, pm, psum, po, lens, ps)
+        pa_prefill_chunk(outp, qp, qsl, 70, pool.k, pool.v, cbt, clens, w.scale, pool.k_scale,
+                         pool.v_scale)
+
+    step()
+    torch.cuda.synchronize()
+    ref, refp = out.clone(), outp.clone()
+    kref, vref = pool.k.clone(), pool.v.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        outp.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "decode output differs on replay %d" % rep
+        assert torch.equal(outp, refp), "prefill output differs on replay %d" % rep
+        # bytes, not values: unowned slots hold NaN patterns
+        assert torch.equal(pool.k.view(torch.uint8), kref.view(torch.uint8))
+        assert torch.equal(pool.v.view(torch.uint8), vref.view(torch.uint8))
+        # unrelated eager work between replays
+        x = torch.randn(1024, 1024, device="cuda")
+        (x @ x).sum().item()

@@ -25,13 +25,14 @@ BS = 16
 def layout_pool(Kc_list, Vc_list, tables, num_blocks, dtype="f32"):
     """Write contiguous per-sequence K/V (storage dtype) into pools.
 
-    K element (seq, pos, h, d) -> k_pool.flat[((blk*Hkv + h)*BS + off)*D + d]
+    K element (seq, pos, h, d) -> k_pool.flat[(((blk*Hkv + h)*(D/X) + d//X)*BS + off)*X + d%X]
     V element (seq, pos, h, d) -> v_pool.flat[((blk*Hkv + h)*D + d)*BS + off]
-    with blk = table[pos // BS], off = pos % BS.  Unowned elements are NaN
-    (f32), 0x7FC0 (bf16) or 0x7F (fp8).
+    with blk = table[pos // BS], off = pos % BS and X = 16 bytes of elements.
+    Unowned elements are NaN (f32), 0x7FC0 (bf16) or 0x7F (fp8).
     """
     hkv, d = Kc_list[0].shape[1], Kc_list[0].shape[2]
     st = pa.STORAGE_DTYPES[dtype]
+    X = 16 // np.dtype(st).itemsize
     poison = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}[dtype]
     kf = np.full(num_blocks * hkv * BS * d, poison, dtype=st)
     vf = np.full(num_blocks * hkv * BS * d, poison, dtype=st)
@@ -40,9 +41,9 @@ def layout_pool(Kc_list, Vc_list, tables, num_blocks, dtype="f32"):
             blk, off = int(tab[pos // BS]), pos % BS
             for h in range(hkv):
                 for dd in range(d):
-                    kf[((blk * hkv + h) * BS + off) * d + dd] = Kc[pos, h, dd]
+                    kf[(((blk * hkv + h) * (d // X) + dd // X) * BS + off) * X + dd % X] = Kc[pos, h, dd]
                     vf[((blk * hkv + h) * d + dd) * BS + off] = Vc[pos, h, dd]
-    return kf.reshape(num_blocks, hkv, BS, d), vf.reshape(num_blocks, hkv, d, BS)
+    return kf.reshape(num_blocks, hkv, d // X, BS, X), vf.reshape(num_blocks, hkv, d, BS)
 
 
 def random_case(rng, lens, hq, hkv, d, num_blocks=None, dist="normal"):
@@ -350,13 +351,14 @@ def test_append_writes_the_layout_and_nothing_else(dtype):
     rng = np.random.default_rng(16)
     nb, hkv, d = 6, 2, 64
     st = pa.STORAGE_DTYPES[dtype]
+    X = 16 // np.dtype(st).itemsize
     if dtype == "f32":
-        kp = rng.standard_normal((nb, hkv, BS, d)).astype(np.float32)
+        kp = rng.standard_normal((nb, hkv, d // X, BS, X)).astype(np.float32)
         vp = rng.standard_normal((nb, hkv, d, BS)).astype(np.float32)
         kn = rng.standard_normal((5, hkv, d)).astype(np.float32)
         vn = rng.standard_normal((5, hkv, d)).astype(np.float32)
     else:
-        kp = rng.integers(0, 65536, (nb, hkv, BS, d)).astype(np.uint16)
+        kp = rng.integers(0, 65536, (nb, hkv, d // X, BS, X)).astype(np.uint16)
         vp = rng.integers(0, 65536, (nb, hkv, d, BS)).astype(np.uint16)
         kn = rng.integers(0, 65536, (5, hkv, d)).astype(np.uint16)
         vn = rng.integers(0, 65536, (5, hkv, d)).astype(np.uint16)
@@ -369,7 +371,7 @@ def test_append_writes_the_layout_and_nothing_else(dtype):
         blk, off = s // BS, s % BS
         for h in range(hkv):
             for dd in range(d):
-                kf[((blk * hkv + h) * BS + off) * d + dd] = kn[t, h, dd]
+                kf[(((blk * hkv + h) * (d // X) + dd // X) * BS + off) * X + dd % X] = kn[t, h, dd]
                 vf[((blk * hkv + h) * d + dd) * BS + off] = vn[t, h, dd]
     assert k2.dtype == st and v2.dtype == st
     assert k2.reshape(-1).tobytes() == kf.tobytes()
@@ -379,7 +381,7 @@ def test_append_writes_the_layout_and_nothing_else(dtype):
 def test_append_fp8_encodes_with_per_head_scale():
     rng = np.random.default_rng(17)
     nb, hkv, d = 3, 2, 64
-    kp = np.zeros((nb, hkv, BS, d), np.uint8)
+    kp = np.zeros((nb, hkv, d // 16, BS, 16), np.uint8)
     vp = np.zeros((nb, hkv, d, BS), np.uint8)
     g = torch.Generator().manual_seed(17)
     kn = torch.randn(4, hkv, d, generator=g).bfloat16()
@@ -397,7 +399,7 @@ def test_append_fp8_encodes_with_per_head_scale():
                 .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
             want_v = torch.from_numpy((vn[t, h].float().numpy() / vs[h]).astype(np.float32)) \
                 .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-            assert np.array_equal(k2[s // BS, h, s % BS], want_k)
+            assert np.array_equal(k2[s // BS, h, :, s % BS, :].reshape(-1), want_k)
             assert np.array_equal(v2[s // BS, h, :, s % BS], want_v)
 
 
@@ -409,7 +411,7 @@ def test_append_then_gather_roundtrips_values():
     kn = rng.standard_normal((L, 2, 64)).astype(np.float32)
     vn = rng.standard_normal((L, 2, 64)).astype(np.float32)
     slots = np.array([table[p // BS] * BS + p % BS for p in range(L)], np.int32)
-    kp = np.full((nb, 2, BS, 64), np.nan, np.float32)
+    kp = np.full((nb, 2, 16, BS, 4), np.nan, np.float32)
     vp = np.full((nb, 2, 64, BS), np.nan, np.float32)
     kp, vp = pa.oracle_append(kp, vp, kn, vn, slots, "f32", "f32")
     K, V = pa.gather_sequence(kp, vp, table, L, "f32")
@@ -418,7 +420,7 @@ def test_append_then_gather_roundtrips_values():
 
 
 def test_gather_refuses_tables_that_do_not_cover_the_context():
-    kp = np.zeros((4, 1, BS, 64), np.float32)
+    kp = np.zeros((4, 1, 16, BS, 4), np.float32)
     vp = np.zeros((4, 1, 64, BS), np.float32)
     with pytest.raises(ValueError):
         pa.gather_sequence(kp, vp, np.array([1, -1], np.int32), 20, "f32")

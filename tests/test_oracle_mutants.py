@@ -74,11 +74,13 @@ def _gather_v_like_k(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_size=16
     K, _ = ORIG_GATHER(k_pool, v_pool, row, L, dt, ks, vs, block_size)
     n = -(-L // block_size)
     ids = np.asarray(row[:n], dtype=np.int64)
-    vb = pa.storage_to_f64(v_pool[ids], dt)                 # read as if [n, Hkv, bs, D]
+    vb = pa.storage_to_f64(v_pool[ids], dt)                 # read as if it had K's layout
     if dt == "fp8":
         vb = vb * np.asarray(vs, np.float64)[None, :, None, None]
-    hkv, d = k_pool.shape[1], k_pool.shape[3]
-    V = vb.reshape(n, hkv, block_size, d).transpose(0, 2, 1, 3).reshape(n * block_size, hkv, d)[:L]
+    hkv, x = k_pool.shape[1], k_pool.shape[4]
+    d = k_pool.shape[2] * x
+    V = vb.reshape(n, hkv, d // x, block_size, x).transpose(0, 3, 1, 2, 4) \
+        .reshape(n * block_size, hkv, d)[:L]
     return K, V
 
 
