@@ -258,7 +258,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, ps),
         },
     }
     if has_prefill:
@@ -268,6 +268,38 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, ms_per_step)
     print(json.dumps(result), flush=True)
+
+
+def decode_source_hash():
+    """sha256 of the decode kernel's sources with comments and blank lines
+    removed (the key under which profiles/ stores measured HBM traffic)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_234_amd", "csrc")
+    for f in ("pa_decode.hip", "pa_tiles.hpp", "pa_device.hpp", "pa_internal.hpp"):
+        with open(os.path.join(csrc, f)) as fh:
+            lines = [re.sub(r"//.*", "", ln).rstrip() for ln in fh.read().splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, ps):
+    """HBM bytes per decode launch from the FETCH_SIZE / WRITE_SIZE counter
+    runs summarised under profiles/ (copy-calibrated), or None when no
+    summary matches this workload, partition size and decode source."""
+    import glob
+    want = {"workload": workload, "partition_size": str(ps), "decode_source_sha256": decode_source_hash()}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.md"))):
+        kv = {}
+        with open(path) as fh:
+            for ln in fh:
+                if ":" in ln and not ln.startswith(("|", "#", " ")):
+                    k, v = ln.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if all(kv.get(k) == v for k, v in want.items()) and "traffic_bytes_per_launch" in kv:
+            return int(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(w, budget_s, gpu_ms):

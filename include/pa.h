@@ -6,31 +6,39 @@
  * engines around (InferX, infer-lab, llm-infer, RustInfer):
  *
  *   pa_kv_append             write this step's new K/V rows into their pool
- *                            slots (llm-infer, "What It Does": the per-layer
- *                            graph holds "KV writes" and attention; InferX,
- *                            "The kernels underneath": fp8 e4m3 KV writes
- *                            with per-layer scales frozen at warm-up).
+ *                            slots (llm-infer, "What It Does": the captured
+ *                            per-layer decode graph writes the KV cache next
+ *                            to attention; InferX, "The kernels underneath":
+ *                            an fp8 e4m3 KV cache whose per-layer scales are
+ *                            fixed during warm-up).
  *   pa_decode                grouped-query softmax(scale * q K^T) V for one
  *                            query token per sequence, K/V gathered through
  *                            per-sequence block tables (infer-lab, technique
- *                            table: "PagedAttention -- block allocator, block
- *                            tables, refcounting"; llm-infer, "What It Does":
- *                            "Paged KV cache with block tables").  Blocks
- *                            may be shared by several sequences (infer-lab,
- *                            RadixAttention row; llm-infer, prefix caching).
- *                            With partition_size > 0 it computes split-K
- *                            partials instead (flash-decoding).
+ *                            table, PagedAttention row: a block allocator,
+ *                            block tables and reference counts; llm-infer,
+ *                            "What It Does": a paged KV cache addressed by
+ *                            block tables).  Blocks may be shared by several
+ *                            sequences (infer-lab, RadixAttention row;
+ *                            llm-infer, prefix caching).  With
+ *                            partition_size > 0 it computes split-K partials
+ *                            instead (flash-decoding).
  *   pa_decode_splitk_reduce  merge those partials into the output.
  *   pa_prefill_chunk         causal attention of prefill chunks over their
  *                            cached prefix (InferX, "Status": chunked
- *                            prefill; infer-lab, "chunked prefill ==
- *                            one-shot prefill"; llm-infer, "ragged batched
- *                            prefill").
+ *                            prefill; infer-lab, invariants: prefilling in
+ *                            chunks gives the one-shot result; llm-infer,
+ *                            "What It Does": prefill of ragged batches).
  *
  * Conventions (the pages leave these open; the library fixes them):
  *
  *   block size   bs = 16 tokens.  Slot s = block * bs + offset.
- *   K pool       [num_blocks][num_kv_heads][bs][head_dim]
+ *   K pool       [num_blocks][num_kv_heads][head_dim / X][bs][X], X = the
+ *                number of elements in 16 bytes (4 fp32, 8 bf16, 16 fp8):
+ *                element (token t, dim d) of a block-head sits at
+ *                ((d / X) * bs + t) * X + d % X.  Each 16-byte chunk holds X
+ *                consecutive dims of one token; the 16 tokens' chunks of one
+ *                dim group are contiguous, so one wave-wide 16-byte load
+ *                reads 1 KB in a single contiguous run.
  *   V pool       [num_blocks][num_kv_heads][head_dim][bs]   (token-minor)
  *   Q, out       [tokens][num_heads][head_dim], token-major, contiguous
  *   GQA          query head hq reads KV head hq / G, G = num_heads / num_kv_heads
@@ -47,8 +55,8 @@
  *
  * Supported (q dtype, cache dtype): (F32, F32), (BF16, BF16), (BF16, FP8).
  * head_dim in {64, 128}; block_size == 16; num_heads % num_kv_heads == 0 and
- * 1 <= G <= 16.  Anything else returns PA_ERR_UNSUPPORTED without launching;
- * there is no fallback path.
+ * 1 <= G <= 16; pa_decode takes batch <= 4096.  Anything else returns
+ * PA_ERR_UNSUPPORTED without launching; there is no fallback path.
  *
  * Ownership and errors.  Every pointer is device memory owned by the caller;
  * the library allocates nothing, frees nothing and keeps no state between

@@ -1,9 +1,9 @@
 // Paged decode attention for gfx950: persistent wave streaming.
 //
 // Operation: grouped-query softmax(scale * q K^T) V for one query token per
-// sequence, over a paged cache (infer-lab: technique table "PagedAttention",
-// layout section "GQA", tiled online-softmax attention; llm-infer: "What It
-// Does", paged KV cache with block tables; the tiling follows the
+// sequence, over a paged cache (infer-lab: technique table, PagedAttention
+// row; layout section, GQA; tiled online-softmax attention; llm-infer, "What
+// It Does": a paged KV cache with block tables; the tiling follows the
 // FlashAttention-2 reference llm-infer cites).  With partition_size > 0 the
 // context is cut into fixed partitions whose softmax partials (m, l, o) are
 // merged by pa_decode_splitk_reduce (flash-decoding split-K).

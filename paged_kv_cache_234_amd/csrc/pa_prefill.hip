@@ -2,9 +2,9 @@
 //
 // A chunk of C query tokens starting after P cached tokens (context length
 // L = P + C, its own K/V already appended) attends causally: query i, at
-// position P + i, sees keys 0 .. P + i (InferX "Status": chunked prefill;
-// infer-lab: "chunked prefill == one-shot prefill"; llm-infer "What It
-// Does": ragged batched prefill with optional chunking).
+// position P + i, sees keys 0 .. P + i (InferX, "Status": chunked prefill;
+// infer-lab, invariants: prefilling in chunks gives the one-shot result;
+// llm-infer, "What It Does": prefill of ragged batches, optionally chunked).
 //
 // Work decomposition: the 16 MFMA columns of a wavefront's query tile are
 // npos = 16 / G consecutive query positions times the G query heads of one KV
