@@ -54,11 +54,26 @@ struct DecodeArgs {
 template <int KIND> struct QType { using T = uint16_t; };
 template <> struct QType<kF32> { using T = float; };
 
-// Items per KV head of a sequence of context length L.
+// Partitions (items) per KV head of a sequence of context length L.
 __device__ __forceinline__ int items_of(const DecodeArgs& a, int L) {
     if (L <= 0) return 0;
     return a.split ? (L + a.partition_size - 1) / a.partition_size : 1;
 }
+
+// Tiles per KV head of a sequence: full items hold tpi tiles, the last one
+// the tiles its remaining positions need.
+__device__ __forceinline__ int tiles_of(const DecodeArgs& a, int L, int tt, int tpi) {
+    const int n = items_of(a, L);
+    if (n == 0) return 0;
+    return (n - 1) * tpi + (L - (n - 1) * a.partition_size + tt - 1) / tt;
+}
+
+// Online-softmax state of one wavefront's piece of an item, parked in LDS
+// until the wavefront owning the item's first tile merges it.
+template <int NVT> struct SegSlot {
+    f32x4 o[NVT][kWave];
+    float m[kWave], mr[kWave], l[kWave];
+};
 
 template <int KIND, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
@@ -68,16 +83,18 @@ void decode_kernel(DecodeArgs a) {
     constexpr int TT = Ops::TT, TB = Ops::TB, NVT = Ops::NVT, ELEM = Ops::ELEM;
     constexpr int NT = NW * kWave;
 
-    __shared__ int s_pre[kMaxDecodeBatch + 1];   // exclusive prefix of items per head
     __shared__ int s_len[kMaxDecodeBatch];       // context lengths
-    __shared__ int s_scan[NT];
+    __shared__ int s_tpre[kMaxDecodeBatch + 1];  // exclusive prefix of tiles per KV head
+    __shared__ int s_wsum[NW];
+    __shared__ SegSlot<NVT> s_seg[NW][2];        // [wave][0: first piece, 1: last piece]
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int B = a.batch;
+    const int tpi = (a.partition_size + TT - 1) / TT;     // tiles of a full item
 
-    // ---- prefix of per-sequence item counts (each thread: a run of sequences)
+    // ---- prefix of per-sequence tile counts (each thread: a run of sequences)
     const int per = (B + NT - 1) / NT;
     const int bs0 = tid * per;
     int local = 0;
@@ -85,26 +102,32 @@ void decode_kernel(DecodeArgs a) {
         if (bs0 + k < B) {
             const int L = a.context_lens[bs0 + k];
             s_len[bs0 + k] = L;
-            local += items_of(a, L);
+            local += tiles_of(a, L, TT, tpi);
         }
-    s_scan[tid] = local;
+    int incl = local;                                     // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
+    int wbase = 0, total_tiles = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        wbase += (w < wave) ? s_wsum[w] : 0;
+        total_tiles += s_wsum[w];
     }
     {
-        int run = s_scan[tid] - local;
+        int run = wbase + incl - local;
         for (int k = 0; k < per; ++k)
             if (bs0 + k < B) {
-                s_pre[bs0 + k] = run;
-                run += items_of(a, s_len[bs0 + k]);
+                s_tpre[bs0 + k] = run;
+                run += tiles_of(a, s_len[bs0 + k], TT, tpi);
             }
-        if (tid == 0) s_pre[B] = s_scan[NT - 1];
+        if (tid == 0) s_tpre[B] = total_tiles;
     }
-    // single pass: sequences with L = 0 have no item; their rows are zeros
+    // single pass: sequences with L = 0 have no tile; their rows are zeros
     if (!a.split) {
         const long rows = (long)B * a.num_heads * D;
         for (long r = (long)blockIdx.x * NT + tid; r < rows; r += (long)gridDim.x * NT) {
@@ -116,112 +139,121 @@ void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ---- this wavefront's item range -----------------------------------------
+    // ---- tile ranges ----------------------------------------------------------
+    // Tiles are numbered b-major, then KV head, then position.  Workgroup k
+    // takes the items whose first tile lies in [T k / NWG, T (k+1) / NWG): a
+    // range of whole items of about T / NWG tiles.  Its NW wavefronts split
+    // that range into NW equal runs of tiles, cutting items where they must.
     const int Hkv = a.num_kv_heads;
-    const long total = (long)Hkv * s_pre[B];
-    const long W = (long)gridDim.x * NW;
-    const long gw = (long)blockIdx.x * NW + wave;
-    const long i0 = total * gw / W, i1 = total * (gw + 1) / W;
-    if (i0 >= i1) return;
-    const long nitems = i1 - i0;
+    const long T = (long)Hkv * total_tiles;
 
-    // first item: the sequence b with Hkv*pre[b] <= i0 < Hkv*pre[b+1]
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((long)Hkv * s_pre[mid] <= i0) lo = mid; else hi = mid - 1;
-    }
+    // sequence b with Hkv*tpre[b] <= g < Hkv*tpre[b+1] (g < T): the largest
+    // such b, searched 64 candidates at a time (two LDS round trips for 4096
+    // sequences).  tpre is nondecreasing, so the lanes whose candidate
+    // qualifies form a prefix of the wave.
+    auto seq_of = [&](long g) {
+        int lo = 0, span = B;
+        while (span > 1) {
+            const int stride = (span + kWave - 1) / kWave;
+            const int idx = lo + lane * stride;
+            const bool ok = idx < lo + span && (long)Hkv * s_tpre[idx] <= g;
+            const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));
+            const int end = lo + span;
+            lo += (cnt - 1) * stride;
+            span = min(stride, end - lo);
+        }
+        return lo;
+    };
+    // first tile of the first item starting at or after tile g
+    auto item_start_at_or_after = [&](long g) -> long {
+        if (g >= T) return T;
+        const int b = seq_of(g);
+        const int tb = s_tpre[b + 1] - s_tpre[b];
+        const long base = (long)Hkv * s_tpre[b];
+        const int h = (int)((g - base) / tb);
+        const int j = (int)(g - base - (long)h * tb);
+        const int p = (j + tpi - 1) / tpi;
+        if (p < items_of(a, s_len[b])) return base + (long)h * tb + (long)p * tpi;
+        return base + (long)(h + 1) * tb;
+    };
+    const long nwg = gridDim.x;
+    const long wg_a = item_start_at_or_after(T * (long)blockIdx.x / nwg);
+    const long wg_e = item_start_at_or_after(T * ((long)blockIdx.x + 1) / nwg);
+    auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
+    const long g0 = wave_start(wave), g1 = wave_start(wave + 1);
+    const int ntiles = (int)(g1 - g0);
 
     const int g = lane & 15, grp = lane >> 4;
     const long head_stride = (long)kBlock * D * ELEM;              // one (block, head) tile
     const long blk_stride = head_stride * Hkv;
 
-    // Item cursor: (b, h, p), items per head n of sequence b, token range [tb, te).
-    struct Item {
-        int b, h, p, n, tb, te, nt;
+    // Tile cursor: sequence b, KV head h, item p, tile jj of the item; the
+    // item covers positions [tb, te) in nti tiles; t0 is its first tile's
+    // global number.
+    struct Cursor {
+        int b, h, p, jj, n, tb, te, nti;
+        long t0;
     };
-    auto set_item = [&](Item& it, int b, int h, int p) {
-        it.b = b;
-        it.h = h;
-        it.p = p;
-        it.n = s_pre[b + 1] - s_pre[b];
-        it.tb = p * a.partition_size;
-        it.te = min(s_len[b], it.tb + a.partition_size);
-        it.nt = (it.te - it.tb + TT - 1) / TT;
+    auto set_item = [&](Cursor& c, int b, int h, int p, long t0) {
+        c.b = b;
+        c.h = h;
+        c.p = p;
+        c.n = items_of(a, s_len[b]);
+        c.tb = p * a.partition_size;
+        c.te = min(s_len[b], c.tb + a.partition_size);
+        c.nti = (c.te - c.tb + TT - 1) / TT;
+        c.t0 = t0;
     };
-    // only called while another item of this wavefront's range exists
-    auto next_item = [&](Item& it) {
-        int b = it.b, h = it.h, p = it.p + 1;
-        if (p == it.n) {
+    // only called while another tile of this wavefront's run exists
+    auto advance = [&](Cursor& c) {
+        if (++c.jj < c.nti) return;
+        const long t0 = c.t0 + c.nti;
+        int b = c.b, h = c.h, p = c.p + 1;
+        if (p == c.n) {
             p = 0;
             if (++h == Hkv) {
                 h = 0;
-                do { ++b; } while (s_pre[b + 1] == s_pre[b]);    // skip L = 0 sequences
+                do { ++b; } while (s_tpre[b + 1] == s_tpre[b]);    // skip L = 0 sequences
             }
         }
-        set_item(it, b, h, p);
+        c.jj = 0;
+        set_item(c, b, h, p, t0);
     };
 
-    Item ci;   // item being computed
-    {
-        const long r = i0 - (long)Hkv * s_pre[lo];
-        const int n = s_pre[lo + 1] - s_pre[lo];
-        set_item(ci, lo, (int)(r / n), (int)(r % n));
+    Cursor cc;          // tile being computed
+    if (ntiles > 0) {
+        const int b = seq_of(g0);
+        const int tb = s_tpre[b + 1] - s_tpre[b];
+        const long base = (long)Hkv * s_tpre[b];
+        const int h = (int)((g0 - base) / tb);
+        const int j = (int)(g0 - base - (long)h * tb);
+        const int p = j / tpi;
+        set_item(cc, b, h, p, base + (long)h * tb + (long)p * tpi);
+        cc.jj = j - p * tpi;
     }
-    Item li = ci;          // item of the tile being loaded (one tile ahead)
-    int ln = 0;            // tile index within li
-    long lcount = 1;       // items entered by the load cursor
-    bool lvalid = true;
+    bool tail_open = false;       // this wave's last piece ends inside its item
+    Cursor tail_item;
 
-    // block ids of the load cursor's tile, fetched one tile ahead
-    int phys[TB];
-    auto fetch_ids = [&]() {
-        const int32_t* bt = a.block_tables + (long)li.b * a.max_blocks_per_seq;
-        const int lb = (li.tb + ln * TT) / kBlock;
-        const int last = (li.te - 1) / kBlock;
-#pragma unroll
-        for (int j = 0; j < TB; ++j) phys[j] = bt[min(lb + j, last)];
-    };
-    auto issue = [&](typename Ops::Regs& r) {
-        const long hoff = (long)li.h * head_stride;
-        Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, phys, lane);
-    };
-    auto advance_load = [&]() {
-        if (++ln == li.nt) {
-            ln = 0;
-            if (lcount == nitems) {
-                lvalid = false;
-                return;
-            }
-            ++lcount;
-            next_item(li);
-        }
-        fetch_ids();
-    };
-
-    // per-item compute state
+    WaveSoftmax<KIND, D> st;
     typename Ops::Q qop[1];
     float c = a.scale_log2;
     auto load_q = [&]() {
-        const int hq = ci.h * a.group + g;
-        const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((long)ci.b * a.num_heads + hq) * D;
+        const int hq = cc.h * a.group + g;
+        const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((long)cc.b * a.num_heads + hq) * D;
         Ops::load_q(qop[0], qrow, g < a.group, lane);
         c = a.scale_log2;
-        if (KIND == kFP8) c *= a.k_scale[ci.h];
+        if (KIND == kFP8) c *= a.k_scale[cc.h];
     };
-    WaveSoftmax<KIND, D> st;
-    st.init();
-    int cn = 0;            // tile index within ci
-    long ccount = 1;       // items entered by the compute cursor
 
-    auto finish_item = [&]() {
+    // write an item's result from st: a split-K partial, or the output rows
+    auto finish_item = [&](const Cursor& it) {
         const float lt = sum_over_groups(st.l[0]);          // against the reference mr
         if (g < a.group) {
-            const int hq = ci.h * a.group + g;
-            const float vs = (KIND == kFP8) ? a.v_scale[ci.h] : 1.0f;
+            const int hq = it.h * a.group + g;
+            const float vs = (KIND == kFP8) ? a.v_scale[it.h] : 1.0f;
             const float inv = vs / lt;
             if (a.split) {
-                const long pi = ((long)ci.b * a.num_heads + hq) * a.max_partitions + ci.p;
+                const long pi = ((long)it.b * a.num_heads + hq) * a.max_partitions + it.p;
                 float* po = a.part_out + pi * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t)
@@ -231,7 +263,7 @@ void decode_kernel(DecodeArgs a) {
                     a.part_sum[pi] = lt * fast_exp2(st.mr[0] - st.m[0]);   // against the true max
                 }
             } else {
-                const long oi = ((long)ci.b * a.num_heads + hq) * D;
+                const long oi = ((long)it.b * a.num_heads + hq) * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t) {
                     const f32x4 v = st.o[0][t] * inv;
@@ -246,45 +278,106 @@ void decode_kernel(DecodeArgs a) {
             }
         }
     };
-    auto compute = [&](typename Ops::Regs& r) {
-        const int nvalid = ci.te - (ci.tb + cn * TT);
-        const int nolimit[1] = {TT};
-        st.step(r, qop, c, nvalid, nolimit, nvalid < TT, lane);
-        if (++cn == ci.nt) {
-            finish_item();
-            cn = 0;
-            if (ccount < nitems) {
-                ++ccount;
-                const int ob = ci.b, oh = ci.h;
-                next_item(ci);
-                st.init();
-                if (ci.b != ob || ci.h != oh) load_q();
-            }
-        }
+    auto park = [&](SegSlot<NVT>& s) {
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) s.o[t][lane] = st.o[0][t];
+        s.m[lane] = st.m[0];
+        s.mr[lane] = st.mr[0];
+        s.l[lane] = st.l[0];
     };
 
-    load_q();
-    fetch_ids();
-    typename Ops::Regs ra, rb;
-    issue(ra);
-    advance_load();
-    while (true) {
-        if (lvalid) {
-            issue(rb);
-            advance_load();
-            compute(ra);
-        } else {
-            compute(ra);
-            break;
+    if (ntiles > 0) {
+        Cursor lc = cc;     // tile being loaded (one ahead)
+        int nloaded = 0;
+        int phys[TB];
+        auto fetch_ids = [&]() {
+            const int32_t* bt = a.block_tables + (long)lc.b * a.max_blocks_per_seq;
+            const int lb = (lc.tb + lc.jj * TT) / kBlock;
+            const int last = (lc.te - 1) / kBlock;
+#pragma unroll
+            for (int j = 0; j < TB; ++j) phys[j] = bt[min(lb + j, last)];
+        };
+        auto issue = [&](typename Ops::Regs& r) {
+            const long hoff = (long)lc.h * head_stride;
+            Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, phys, lane);
+            if (++nloaded < ntiles) {
+                advance(lc);
+                fetch_ids();
+            }
+        };
+        int ncomputed = 0;
+        bool piece_from_start = cc.jj == 0;
+        auto compute = [&](typename Ops::Regs& r) {
+            const int nvalid = cc.te - (cc.tb + cc.jj * TT);
+            const int nolimit[1] = {TT};
+            st.step(r, qop, c, nvalid, nolimit, nvalid < TT, lane);
+            ++ncomputed;
+            const bool item_done = cc.jj + 1 == cc.nti;
+            const bool run_done = ncomputed == ntiles;
+            if (item_done || run_done) {
+                if (piece_from_start && item_done) {
+                    finish_item(cc);
+                } else if (!piece_from_start) {
+                    park(s_seg[wave][0]);           // continues an item of the previous wave
+                } else {
+                    tail_open = true;               // continued by the next wave(s)
+                    tail_item = cc;
+                }
+                if (!run_done) {
+                    const int ob = cc.b, oh = cc.h;
+                    advance(cc);
+                    piece_from_start = true;
+                    if (!tail_open) st.init();
+                    if (cc.b != ob || cc.h != oh) load_q();
+                }
+            } else {
+                advance(cc);
+            }
+        };
+
+        st.init();
+        load_q();
+        fetch_ids();
+        typename Ops::Regs ra, rb;
+        issue(ra);
+        while (true) {
+            if (nloaded < ntiles) {
+                issue(rb);
+                compute(ra);
+            } else {
+                compute(ra);
+                break;
+            }
+            if (nloaded < ntiles) {
+                issue(ra);
+                compute(rb);
+            } else {
+                compute(rb);
+                break;
+            }
         }
-        if (lvalid) {
-            issue(ra);
-            advance_load();
-            compute(rb);
-        } else {
-            compute(rb);
-            break;
+    }
+
+    // ---- merge items cut between wavefronts --------------------------------
+    __syncthreads();
+    if (tail_open) {
+        const long item_end = tail_item.t0 + tail_item.nti;
+        for (int w = wave + 1; w < NW; ++w) {
+            const long s0 = wave_start(w), s1 = wave_start(w + 1);
+            if (s0 >= item_end) break;
+            if (s1 == s0) continue;
+            const SegSlot<NVT>& s = s_seg[w][0];
+            const float mr2 = s.mr[lane];
+            const float mnew = fmaxf(st.mr[0], mr2);
+            const float a1 = st.mr[0] == mnew ? 1.f : fast_exp2(st.mr[0] - mnew);
+            const float a2 = mr2 == mnew ? 1.f : fast_exp2(mr2 - mnew);
+            st.mr[0] = mnew;
+            st.m[0] = fmaxf(st.m[0], s.m[lane]);
+            st.l[0] = st.l[0] * a1 + s.l[lane] * a2;
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) st.o[0][t] = st.o[0][t] * a1 + s.o[t][lane] * a2;
         }
+        finish_item(tail_item);
     }
 }
 
@@ -295,9 +388,10 @@ static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     // every workgroup resident at once: CUs x (waves per SIMD) workgroups of 4 waves
-    const long max_items = (long)a.batch * a.num_kv_heads * a.max_partitions;
+    const long tpi = (a.partition_size + TileOps<KIND, D>::TT - 1) / TileOps<KIND, D>::TT;
+    const long max_tiles = (long)a.batch * a.num_kv_heads * a.max_partitions * tpi;
     long grid = (long)cus * waves_per_simd(KIND, D);
-    grid = std::min(grid, (max_items + NW - 1) / NW);
+    grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
     hipLaunchKernelGGL((decode_kernel<KIND, D, NW>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
