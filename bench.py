@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="decode prefix-sharing batches with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--eager", action="store_true",
                     help="launch the kernels one by one instead of replaying captured graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -59,8 +61,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_splitk_reduce,
-                                        pa_prefill_chunk, pa_selftest)
+    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_cascade,
+                                        pa_decode_splitk_reduce, pa_prefill_chunk, pa_selftest)
     from workloads import make_config
 
     dev = "cuda:0"
@@ -91,6 +93,16 @@ def main():
     part_sum = torch.empty((B, hq, pmax), device=dev)
     part_out = torch.empty((B, hq, pmax, d), device=dev)
     out = torch.empty_like(q)
+    # prefix groups: the shared blocks are read once per group (cascade)
+    cascade = bool(w.prefix_groups) and ps > 0 and not args.no_cascade
+    if cascade:
+        g_start, g_seqs, g_plens = [0], [], []
+        for members, nshared in w.prefix_groups:
+            g_seqs.extend(int(b) for b in members)
+            g_start.append(len(g_seqs))
+            g_plens.append(int(nshared) * w.block_size)
+        g_start, g_seqs, g_plens = i32(g_start), i32(g_seqs), i32(g_plens)
+        g_max = max(len(m) for m, _ in w.prefix_groups)
     has_prefill = w.num_chunks > 0
     if has_prefill:
         qp = w.q_prefill.contiguous()
@@ -109,12 +121,7 @@ def main():
         pool.append(new_k, new_v, new_slots)
         if ev is not None:
             ev[1].record(stream)
-        if ps > 0:
-            pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
-                      partition_size=ps, max_partitions=pmax, part_max=part_max,
-                      part_sum=part_sum, part_out=part_out)
-        else:
-            pa_decode(out, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale)
+        decode_only(layer)
         if ev is not None:
             ev[2].record(stream)
         if ps > 0:
@@ -129,7 +136,10 @@ def main():
 
     def decode_only(layer):
         pool = pools[layer % R]
-        if ps > 0:
+        if cascade:
+            pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, g_start, g_seqs, g_plens, g_max,
+                              ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale)
+        elif ps > 0:
             pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
                       partition_size=ps, max_partitions=pmax, part_max=part_max,
                       part_sum=part_sum, part_out=part_out)
@@ -241,6 +251,7 @@ def main():
             "context_tokens": int(w.context_lens.sum()), "new_tokens": int(len(w.new_slots)),
             "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
             "pool_blocks": w.num_blocks, "layer_copies": R,
+            "decode_entry": "pa_decode_cascade" if cascade else "pa_decode",
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 3),
         "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),

@@ -136,6 +136,46 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
                       hipStream_t stream);
 
 /*
+ * Shared-prefix ("cascade") split-K decode: the same partials as pa_decode
+ * with partition_size > 0, for a batch in which prefix groups of sequences
+ * share their first tokens in the same physical blocks (infer-lab, technique
+ * table, RadixAttention row: prefix reuse across requests; llm-infer, "What
+ * It Does": prefix caching; InferX, "Status": a radix prefix cache;
+ * RustInfer, "Architecture": the scheduler's RadixTree prefix cache).  The
+ * whole partitions of a group's shared prefix are read once per KV head for
+ * up to 16 / G members at a time instead of once per member; every other
+ * partition is computed as pa_decode computes it.  Merge with
+ * pa_decode_splitk_reduce.
+ *   group_start        [num_groups + 1] int32: members of group j are
+ *                      group_seqs[group_start[j] .. group_start[j+1])
+ *   group_seqs         member sequence indices (< batch); a sequence belongs
+ *                      to at most one group
+ *   group_prefix_lens  [num_groups] int32: positions 0 .. P_j - 1 of every
+ *                      member are the same tokens in the same blocks (the
+ *                      members' block-table rows agree on the first
+ *                      ceil(P_j / 16) entries) and P_j <= each member's L.
+ *                      Only floor(P_j / partition_size) whole partitions are
+ *                      taken as shared; the rest is read per member.
+ *   max_group_size     host bound on members per group (sizes the grid)
+ * Requires partition_size > 0 (PA_ERR_ARG otherwise) and
+ * batch + num_groups <= 4096 (PA_ERR_UNSUPPORTED otherwise).  num_groups == 0
+ * computes exactly what pa_decode computes.
+ */
+pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
+                              const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch,
+                              const int32_t* group_start, const int32_t* group_seqs,
+                              const int32_t* group_prefix_lens, int32_t num_groups,
+                              int32_t max_group_size,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, float scale,
+                              int32_t partition_size, int32_t max_partitions,
+                              float* part_max, float* part_sum, float* part_out,
+                              hipStream_t stream);
+
+/*
  * Merge split-K partials (the layout pa_decode writes) into out
  * [batch][num_heads][head_dim] of out_dtype (F32 or BF16):
  *   M = max_p m_p,  w_p = l_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p

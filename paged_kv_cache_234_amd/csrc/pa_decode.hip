@@ -8,17 +8,27 @@
 // context is cut into fixed partitions whose softmax partials (m, l, o) are
 // merged by pa_decode_splitk_reduce (flash-decoding split-K).
 //
-// Work decomposition.  A work item is (sequence b, KV head h, partition p):
-// partition_size tokens of one sequence for the whole GQA group of one KV head
-// (G <= 16 query heads form one 16-column MFMA operand, so every K/V byte is
-// read once).  Without split the item is the whole context.  Items are ordered
-// b, h, p and numbered densely (sequences with L = 0 have none); each
-// workgroup first builds the prefix of per-sequence item counts in LDS.  The
-// grid is sized to be resident at once, and wavefront w takes the contiguous
-// item range [I*w/W, I*(w+1)/W).  A wavefront streams the tiles of its items
-// back to back: the next tile's K/V loads -- across item boundaries too --
-// are in flight while the current tile is multiplied, and each finished item
-// writes its partial (or its output) straight from registers.
+// Rows.  The kernel walks a list of rows.  Row b < batch is sequence b: its
+// 16 MFMA columns are the G query heads of one KV head (G <= 16, so every
+// K/V byte is read once per sequence).  The cascade entry point adds one row
+// per prefix group (sequences whose first tokens sit in the same physical
+// blocks, infer-lab RadixAttention row, llm-infer prefix caching): its
+// columns are (member, query head) pairs, 16 / G members at a time, and it
+// covers the whole partitions of the shared prefix once for all members.
+// The members' own rows then skip those partitions.  A group row has one
+// "virtual head" per (KV head, 16-column chunk of members); the chunks of one
+// KV head are adjacent, so they read the same blocks back to back.
+//
+// Work decomposition.  A work item is (row, virtual head, partition).  Tiles
+// of TT positions are numbered row-major, then virtual head, then position;
+// each workgroup builds the prefix of per-row tile counts in LDS.  Workgroup k
+// takes the whole items whose first tile lies in [T k / NWG, T (k+1) / NWG);
+// its NW wavefronts split that run into NW equal runs of tiles.  A wavefront
+// streams its tiles back to back: the next tile's K/V loads -- across item
+// boundaries too -- are in flight while the current tile is multiplied, a
+// finished item writes its partial (or output) straight from registers, and
+// an item cut between wavefronts is merged through LDS by the wavefront that
+// holds its first tile.
 #include <algorithm>
 
 #include "pa_internal.hpp"
@@ -26,7 +36,7 @@
 
 namespace pa {
 
-constexpr int kMaxDecodeBatch = 4096;
+constexpr int kMaxDecodeRows = 4096;
 
 struct DecodeArgs {
     void* out;
@@ -40,6 +50,13 @@ struct DecodeArgs {
     float* part_max;
     float* part_sum;
     float* part_out;
+    // prefix groups (cascade): members of group j are
+    // group_seqs[group_start[j] .. group_start[j+1]), sharing their first
+    // group_prefix_lens[j] positions
+    const int32_t* group_start;
+    const int32_t* group_seqs;
+    const int32_t* group_prefix_lens;
+    int num_groups;
     int max_blocks_per_seq;
     int batch;
     int num_heads;
@@ -53,20 +70,6 @@ struct DecodeArgs {
 
 template <int KIND> struct QType { using T = uint16_t; };
 template <> struct QType<kF32> { using T = float; };
-
-// Partitions (items) per KV head of a sequence of context length L.
-__device__ __forceinline__ int items_of(const DecodeArgs& a, int L) {
-    if (L <= 0) return 0;
-    return a.split ? (L + a.partition_size - 1) / a.partition_size : 1;
-}
-
-// Tiles per KV head of a sequence: full items hold tpi tiles, the last one
-// the tiles its remaining positions need.
-__device__ __forceinline__ int tiles_of(const DecodeArgs& a, int L, int tt, int tpi) {
-    const int n = items_of(a, L);
-    if (n == 0) return 0;
-    return (n - 1) * tpi + (L - (n - 1) * a.partition_size + tt - 1) / tt;
-}
 
 // Online-softmax state of one wavefront's piece of an item, parked in LDS
 // until the wavefront owning the item's first tile merges it.
@@ -83,27 +86,88 @@ void decode_kernel(DecodeArgs a) {
     constexpr int TT = Ops::TT, TB = Ops::TB, NVT = Ops::NVT, ELEM = Ops::ELEM;
     constexpr int NT = NW * kWave;
 
-    __shared__ int s_len[kMaxDecodeBatch];       // context lengths
-    __shared__ int s_tpre[kMaxDecodeBatch + 1];  // exclusive prefix of tiles per KV head
+    // per row: context length; aux = leading partitions covered by the
+    // row's prefix group (sequence rows) or (first member index << 16 |
+    // members) (group rows); exclusive prefix of tiles
+    __shared__ int s_len[kMaxDecodeRows];
+    __shared__ int s_aux[kMaxDecodeRows];
+    __shared__ int s_tpre[kMaxDecodeRows + 1];
     __shared__ int s_wsum[NW];
-    __shared__ SegSlot<NVT> s_seg[NW][2];        // [wave][0: first piece, 1: last piece]
+    __shared__ SegSlot<NVT> s_seg[NW];           // each wave's first piece, if cut
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int B = a.batch;
-    const int tpi = (a.partition_size + TT - 1) / TT;     // tiles of a full item
+    const int R = B + a.num_groups;
+    const int PS = a.partition_size;
+    const int tpi = (PS + TT - 1) / TT;                  // tiles of a full item
+    const int Hkv = a.num_kv_heads;
+    const int mpc = 16 / a.group;                        // group members per 16 columns
 
-    // ---- prefix of per-sequence tile counts (each thread: a run of sequences)
-    const int per = (B + NT - 1) / NT;
-    const int bs0 = tid * per;
+    // ---- row table in LDS -------------------------------------------------------
+    // Group descriptors are read together with the context lengths, and a
+    // group's member list in batches of 8 independent loads, so the prologue
+    // costs two dependent memory round trips.
+    for (int r = tid; r < B; r += NT) {
+        s_len[r] = a.context_lens[r];
+        s_aux[r] = 0;
+    }
+    if (a.num_groups > 0) {
+        constexpr int kBatch = 8;
+        for (int j = tid; j < a.num_groups; j += NT) {
+            const int first = min(max(a.group_start[j], 0), 0x7FFF);
+            const int members = max(0, min(a.group_start[j + 1] - first, 0xFFFF));
+            // whole shared partitions, clamped to the partial buffer and the table row
+            int full = max(0, a.group_prefix_lens[j]) / PS;
+            full = min(full, min(a.max_partitions, a.max_blocks_per_seq * kBlock / PS));
+            s_len[B + j] = members > 0 ? full * PS : 0;
+            s_aux[B + j] = (first << 16) | members;
+        }
+        __syncthreads();                                  // s_len of the sequences
+        for (int j = tid; j < a.num_groups; j += NT) {
+            const int first = s_aux[B + j] >> 16, members = s_aux[B + j] & 0xFFFF;
+            const int full = s_len[B + j] / PS;
+            for (int m0 = 0; m0 < members; m0 += kBatch) {
+                int sq[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    sq[k] = m0 + k < members ? a.group_seqs[first + m0 + k] : -1;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k)
+                    if (sq[k] >= 0 && sq[k] < B)
+                        s_aux[sq[k]] = min(full, (s_len[sq[k]] + PS - 1) / PS);
+            }
+        }
+    }
+    __syncthreads();
+
+    auto row_skip = [&](int r) { return r < B ? s_aux[r] : 0; };
+    auto row_heads = [&](int r) {
+        if (r < B) return Hkv;
+        const int members = s_aux[r] & 0xFFFF;
+        return Hkv * ((members + mpc - 1) / mpc);
+    };
+    auto row_items = [&](int r) {
+        const int L = s_len[r];
+        if (L <= 0) return 0;
+        const int n = a.split ? (L + PS - 1) / PS : 1;
+        return max(0, n - row_skip(r));
+    };
+    // tiles of one (virtual) head of row r
+    auto row_head_tiles = [&](int r) {
+        const int n = row_items(r);
+        if (n == 0) return 0;
+        const int last = row_skip(r) + n - 1;
+        return (n - 1) * tpi + (s_len[r] - last * PS + TT - 1) / TT;
+    };
+
+    // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
+    const int per = (R + NT - 1) / NT;
+    const int r0 = tid * per;
     int local = 0;
     for (int k = 0; k < per; ++k)
-        if (bs0 + k < B) {
-            const int L = a.context_lens[bs0 + k];
-            s_len[bs0 + k] = L;
-            local += tiles_of(a, L, TT, tpi);
-        }
+        if (r0 + k < R) local += row_heads(r0 + k) * row_head_tiles(r0 + k);
     int incl = local;                                     // inclusive scan within the wave
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -121,11 +185,11 @@ void decode_kernel(DecodeArgs a) {
     {
         int run = wbase + incl - local;
         for (int k = 0; k < per; ++k)
-            if (bs0 + k < B) {
-                s_tpre[bs0 + k] = run;
-                run += tiles_of(a, s_len[bs0 + k], TT, tpi);
+            if (r0 + k < R) {
+                s_tpre[r0 + k] = run;
+                run += row_heads(r0 + k) * row_head_tiles(r0 + k);
             }
-        if (tid == 0) s_tpre[B] = total_tiles;
+        if (tid == 0) s_tpre[R] = total_tiles;
     }
     // single pass: sequences with L = 0 have no tile; their rows are zeros
     if (!a.split) {
@@ -140,23 +204,18 @@ void decode_kernel(DecodeArgs a) {
     __syncthreads();
 
     // ---- tile ranges ----------------------------------------------------------
-    // Tiles are numbered b-major, then KV head, then position.  Workgroup k
-    // takes the items whose first tile lies in [T k / NWG, T (k+1) / NWG): a
-    // range of whole items of about T / NWG tiles.  Its NW wavefronts split
-    // that range into NW equal runs of tiles, cutting items where they must.
-    const int Hkv = a.num_kv_heads;
-    const long T = (long)Hkv * total_tiles;
+    const long T = total_tiles;
 
-    // sequence b with Hkv*tpre[b] <= g < Hkv*tpre[b+1] (g < T): the largest
-    // such b, searched 64 candidates at a time (two LDS round trips for 4096
-    // sequences).  tpre is nondecreasing, so the lanes whose candidate
-    // qualifies form a prefix of the wave.
-    auto seq_of = [&](long g) {
-        int lo = 0, span = B;
+    // row r with tpre[r] <= g < tpre[r+1] (g < T): the largest such r,
+    // searched 64 candidates at a time (two LDS round trips for 4096 rows).
+    // tpre is nondecreasing, so the lanes whose candidate qualifies form a
+    // prefix of the wave.
+    auto row_of = [&](long g) {
+        int lo = 0, span = R;
         while (span > 1) {
             const int stride = (span + kWave - 1) / kWave;
             const int idx = lo + lane * stride;
-            const bool ok = idx < lo + span && (long)Hkv * s_tpre[idx] <= g;
+            const bool ok = idx < lo + span && s_tpre[idx] <= g;
             const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));
             const int end = lo + span;
             lo += (cnt - 1) * stride;
@@ -167,14 +226,14 @@ void decode_kernel(DecodeArgs a) {
     // first tile of the first item starting at or after tile g
     auto item_start_at_or_after = [&](long g) -> long {
         if (g >= T) return T;
-        const int b = seq_of(g);
-        const int tb = s_tpre[b + 1] - s_tpre[b];
-        const long base = (long)Hkv * s_tpre[b];
-        const int h = (int)((g - base) / tb);
-        const int j = (int)(g - base - (long)h * tb);
+        const int r = row_of(g);
+        const int th = row_head_tiles(r);
+        const long base = s_tpre[r];
+        const int vh = (int)((g - base) / th);
+        const int j = (int)(g - base - (long)vh * th);
         const int p = (j + tpi - 1) / tpi;
-        if (p < items_of(a, s_len[b])) return base + (long)h * tb + (long)p * tpi;
-        return base + (long)(h + 1) * tb;
+        if (p < row_items(r)) return base + (long)vh * th + (long)p * tpi;
+        return base + (long)(vh + 1) * th;
     };
     const long nwg = gridDim.x;
     const long wg_a = item_start_at_or_after(T * (long)blockIdx.x / nwg);
@@ -187,20 +246,25 @@ void decode_kernel(DecodeArgs a) {
     const long head_stride = (long)kBlock * D * ELEM;              // one (block, head) tile
     const long blk_stride = head_stride * Hkv;
 
-    // Tile cursor: sequence b, KV head h, item p, tile jj of the item; the
-    // item covers positions [tb, te) in nti tiles; t0 is its first tile's
-    // global number.
+    // Tile cursor: row r, virtual head vh (KV head h, member chunk ch), item
+    // p (partition part = p + skip), tile jj of the item; the item covers
+    // positions [tb, te) in nti tiles; t0 is its first tile's global number.
     struct Cursor {
-        int b, h, p, jj, n, tb, te, nti;
+        int r, vh, h, ch, nh, p, part, jj, n, tb, te, nti;
         long t0;
     };
-    auto set_item = [&](Cursor& c, int b, int h, int p, long t0) {
-        c.b = b;
-        c.h = h;
+    auto set_item = [&](Cursor& c, int r, int vh, int p, long t0) {
+        c.r = r;
+        c.vh = vh;
+        c.nh = row_heads(r);
+        const int chunks = c.nh / Hkv;
+        c.h = vh / chunks;
+        c.ch = vh - c.h * chunks;
         c.p = p;
-        c.n = items_of(a, s_len[b]);
-        c.tb = p * a.partition_size;
-        c.te = min(s_len[b], c.tb + a.partition_size);
+        c.part = p + row_skip(r);
+        c.n = row_items(r);
+        c.tb = c.part * PS;
+        c.te = min(s_len[r], c.tb + PS);
         c.nti = (c.te - c.tb + TT - 1) / TT;
         c.t0 = t0;
     };
@@ -208,27 +272,34 @@ void decode_kernel(DecodeArgs a) {
     auto advance = [&](Cursor& c) {
         if (++c.jj < c.nti) return;
         const long t0 = c.t0 + c.nti;
-        int b = c.b, h = c.h, p = c.p + 1;
+        int r = c.r, vh = c.vh, p = c.p + 1;
         if (p == c.n) {
             p = 0;
-            if (++h == Hkv) {
-                h = 0;
-                do { ++b; } while (s_tpre[b + 1] == s_tpre[b]);    // skip L = 0 sequences
+            if (++vh == c.nh) {
+                vh = 0;
+                do { ++r; } while (s_tpre[r + 1] == s_tpre[r]);    // skip rows without tiles
             }
         }
         c.jj = 0;
-        set_item(c, b, h, p, t0);
+        set_item(c, r, vh, p, t0);
+    };
+    // sequence whose block table a row reads: the row's own, or its group's
+    // first member's
+    auto table_seq = [&](int r) {
+        if (r < B) return r;
+        const int sq = load_invariant(a.group_seqs + __builtin_amdgcn_readfirstlane(s_aux[r] >> 16));
+        return (sq >= 0 && sq < B) ? sq : 0;
     };
 
     Cursor cc;          // tile being computed
     if (ntiles > 0) {
-        const int b = seq_of(g0);
-        const int tb = s_tpre[b + 1] - s_tpre[b];
-        const long base = (long)Hkv * s_tpre[b];
-        const int h = (int)((g0 - base) / tb);
-        const int j = (int)(g0 - base - (long)h * tb);
+        const int r = row_of(g0);
+        const int th = row_head_tiles(r);
+        const long base = s_tpre[r];
+        const int vh = (int)((g0 - base) / th);
+        const int j = (int)(g0 - base - (long)vh * th);
         const int p = j / tpi;
-        set_item(cc, b, h, p, base + (long)h * tb + (long)p * tpi);
+        set_item(cc, r, vh, p, base + (long)vh * th + (long)p * tpi);
         cc.jj = j - p * tpi;
     }
     bool tail_open = false;       // this wave's last piece ends inside its item
@@ -237,23 +308,61 @@ void decode_kernel(DecodeArgs a) {
     WaveSoftmax<KIND, D> st;
     typename Ops::Q qop[1];
     float c = a.scale_log2;
-    auto load_q = [&]() {
-        const int hq = cc.h * a.group + g;
-        const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((long)cc.b * a.num_heads + hq) * D;
-        Ops::load_q(qop[0], qrow, g < a.group, lane);
-        c = a.scale_log2;
-        if (KIND == kFP8) c *= a.k_scale[cc.h];
+    int col_seq = -1, col_hq = 0;  // this lane's column: sequence and query head (-1: none)
+    // Q operand, column map and score multiplier of item `it`
+    auto q_for = [&](const Cursor& it, typename Ops::Q& qd, int& cs, int& chq, float& cf) {
+        cs = -1;
+        chq = 0;
+        if (it.r < B) {
+            if (g < a.group) {
+                cs = it.r;
+                chq = it.h * a.group + g;
+            }
+        } else {
+            // this chunk's members, read with scalar loads (no wait on the
+            // K/V loads in flight) and handed to their lanes by select
+            const int aux = __builtin_amdgcn_readfirstlane(s_aux[it.r]);
+            const int first = (aux >> 16) + it.ch * mpc;
+            const int cnt = min(mpc, (aux & 0xFFFF) - it.ch * mpc);
+            const int m = g / a.group;
+            int sq = -1;
+            for (int k = 0; k < cnt; ++k) {
+                const int v = load_invariant(a.group_seqs + first + k);
+                sq = (m == k) ? v : sq;
+            }
+            if (g < mpc * a.group && sq >= 0 && sq < B) {
+                cs = sq;
+                chq = it.h * a.group + g % a.group;
+            }
+        }
+        const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((long)max(cs, 0) * a.num_heads + chq) * D;
+        Ops::load_q(qd, qrow, cs >= 0, lane);
+        cf = a.scale_log2;
+        if (KIND == kFP8) cf *= load_invariant(a.k_scale + it.h);
     };
+    // The load cursor enters each item (row, virtual head) one or two tiles
+    // before the compute cursor does; the item's Q operand is loaded then,
+    // into one prefetch slot, so its latency stays off the compute path.  The
+    // slot holds one item: when the load cursor enters a second item before
+    // the compute cursor has taken the first (one-tile items), that second
+    // item's Q is loaded when the compute cursor reaches it.  Items are
+    // numbered in the order both cursors enter them.
+    // The prefetch is issued before the K/V loads of the tile ahead of the
+    // item: those loads are complete before that tile is multiplied, so the
+    // prefetched operand is complete when the compute cursor takes it.
+    typename Ops::Q qnext;
+    int next_seq = -1, next_hq = 0, next_ord = -1;
+    float next_c = 0.f;
+    int load_ord = 0, comp_ord = 0;
 
     // write an item's result from st: a split-K partial, or the output rows
     auto finish_item = [&](const Cursor& it) {
         const float lt = sum_over_groups(st.l[0]);          // against the reference mr
-        if (g < a.group) {
-            const int hq = it.h * a.group + g;
-            const float vs = (KIND == kFP8) ? a.v_scale[it.h] : 1.0f;
+        if (col_seq >= 0) {
+            const float vs = (KIND == kFP8) ? load_invariant(a.v_scale + it.h) : 1.0f;
             const float inv = vs / lt;
             if (a.split) {
-                const long pi = ((long)it.b * a.num_heads + hq) * a.max_partitions + it.p;
+                const long pi = ((long)col_seq * a.num_heads + col_hq) * a.max_partitions + it.part;
                 float* po = a.part_out + pi * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t)
@@ -263,7 +372,7 @@ void decode_kernel(DecodeArgs a) {
                     a.part_sum[pi] = lt * fast_exp2(st.mr[0] - st.m[0]);   // against the true max
                 }
             } else {
-                const long oi = ((long)it.b * a.num_heads + hq) * D;
+                const long oi = ((long)col_seq * a.num_heads + col_hq) * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t) {
                     const f32x4 v = st.o[0][t] * inv;
@@ -290,20 +399,35 @@ void decode_kernel(DecodeArgs a) {
         Cursor lc = cc;     // tile being loaded (one ahead)
         int nloaded = 0;
         int phys[TB];
+        const int32_t* bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
         auto fetch_ids = [&]() {
-            const int32_t* bt = a.block_tables + (long)lc.b * a.max_blocks_per_seq;
-            const int lb = (lc.tb + lc.jj * TT) / kBlock;
-            const int last = (lc.te - 1) / kBlock;
+            const int lb = __builtin_amdgcn_readfirstlane((lc.tb + lc.jj * TT) / kBlock);
+            const int last = __builtin_amdgcn_readfirstlane((lc.te - 1) / kBlock);
 #pragma unroll
-            for (int j = 0; j < TB; ++j) phys[j] = bt[min(lb + j, last)];
+            for (int j = 0; j < TB; ++j) phys[j] = load_invariant(bt + min(lb + j, last));
         };
+        // load the tile under the load cursor and move the cursor on; the
+        // next tile's block ids and (entering an item) Q go out first
         auto issue = [&](typename Ops::Regs& r) {
             const long hoff = (long)lc.h * head_stride;
-            Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, phys, lane);
+            int ph[TB];
+#pragma unroll
+            for (int j = 0; j < TB; ++j) ph[j] = phys[j];
             if (++nloaded < ntiles) {
+                const int orow = lc.r, ovh = lc.vh;
                 advance(lc);
+                if (lc.r != orow)
+                    bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
                 fetch_ids();
+                if (lc.r != orow || lc.vh != ovh) {
+                    ++load_ord;
+                    if (next_ord <= comp_ord) {
+                        q_for(lc, qnext, next_seq, next_hq, next_c);
+                        next_ord = load_ord;
+                    }
+                }
             }
+            Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, ph, lane);
         };
         int ncomputed = 0;
         bool piece_from_start = cc.jj == 0;
@@ -318,17 +442,26 @@ void decode_kernel(DecodeArgs a) {
                 if (piece_from_start && item_done) {
                     finish_item(cc);
                 } else if (!piece_from_start) {
-                    park(s_seg[wave][0]);           // continues an item of the previous wave
+                    park(s_seg[wave]);              // continues an item of the previous wave
                 } else {
                     tail_open = true;               // continued by the next wave(s)
                     tail_item = cc;
                 }
                 if (!run_done) {
-                    const int ob = cc.b, oh = cc.h;
+                    const int orow = cc.r, ovh = cc.vh;
                     advance(cc);
                     piece_from_start = true;
-                    if (!tail_open) st.init();
-                    if (cc.b != ob || cc.h != oh) load_q();
+                    st.init();
+                    if (cc.r != orow || cc.vh != ovh) {
+                        if (++comp_ord == next_ord) {
+                            qop[0] = qnext;
+                            col_seq = next_seq;
+                            col_hq = next_hq;
+                            c = next_c;
+                        } else {
+                            q_for(cc, qop[0], col_seq, col_hq, c);
+                        }
+                    }
                 }
             } else {
                 advance(cc);
@@ -336,7 +469,7 @@ void decode_kernel(DecodeArgs a) {
         };
 
         st.init();
-        load_q();
+        q_for(cc, qop[0], col_seq, col_hq, c);
         fetch_ids();
         typename Ops::Regs ra, rb;
         issue(ra);
@@ -366,7 +499,7 @@ void decode_kernel(DecodeArgs a) {
             const long s0 = wave_start(w), s1 = wave_start(w + 1);
             if (s0 >= item_end) break;
             if (s1 == s0) continue;
-            const SegSlot<NVT>& s = s_seg[w][0];
+            const SegSlot<NVT>& s = s_seg[w];
             const float mr2 = s.mr[lane];
             const float mnew = fmaxf(st.mr[0], mr2);
             const float a1 = st.mr[0] == mnew ? 1.f : fast_exp2(st.mr[0] - mnew);
@@ -382,14 +515,12 @@ void decode_kernel(DecodeArgs a) {
 }
 
 template <int KIND, int D>
-static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
     constexpr int NW = 4;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // every workgroup resident at once: CUs x (waves per SIMD) workgroups of 4 waves
-    const long tpi = (a.partition_size + TileOps<KIND, D>::TT - 1) / TileOps<KIND, D>::TT;
-    const long max_tiles = (long)a.batch * a.num_kv_heads * a.max_partitions * tpi;
+    // one workgroup of 4 waves per CU and wave slot; fewer for small problems
     long grid = (long)cus * waves_per_simd(KIND, D);
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
@@ -398,27 +529,40 @@ static hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-}  // namespace pa
+// items_bound: an upper bound on (row, virtual head, partition) items
+static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int head_dim,
+                              long items_bound, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    const int kind = cache_kind(cache_dtype);
+    auto tiles = [&](int tt) { return items_bound * ((a.partition_size + tt - 1) / tt); };
+    if (kind == kBF16 && head_dim == 128) e = launch_decode<kBF16, 128>(a, tiles(32), stream);
+    else if (kind == kBF16 && head_dim == 64) e = launch_decode<kBF16, 64>(a, tiles(32), stream);
+    else if (kind == kFP8 && head_dim == 128) e = launch_decode<kFP8, 128>(a, tiles(64), stream);
+    else if (kind == kFP8 && head_dim == 64) e = launch_decode<kFP8, 64>(a, tiles(64), stream);
+    else if (kind == kF32 && head_dim == 128) e = launch_decode<kF32, 128>(a, tiles(16), stream);
+    else if (kind == kF32 && head_dim == 64) e = launch_decode<kF32, 64>(a, tiles(16), stream);
+    else return PA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
-using namespace pa;
-
-extern "C" pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype, const void* k_cache,
-                                 const void* v_cache, pa_dtype_t cache_dtype, const float* k_scale,
-                                 const float* v_scale, const int32_t* block_tables,
-                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                 int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, float scale,
-                                 int32_t partition_size, int32_t max_partitions, float* part_max,
-                                 float* part_sum, float* part_out, hipStream_t stream) {
+// Validation and argument packing shared by pa_decode and pa_decode_cascade.
+static pa_status_t pack_decode(DecodeArgs& a, void* out, const void* q, pa_dtype_t q_dtype,
+                               const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t batch, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               float scale, int32_t partition_size, int32_t max_partitions,
+                               float* part_max, float* part_sum, float* part_out) {
     pa_status_t st = check_attention_shape(q_dtype, cache_dtype, k_scale, v_scale, num_heads,
                                            num_kv_heads, head_dim, block_size);
     if (st != PA_OK) return st;
     if (batch < 0 || max_blocks_per_seq < 1 || partition_size < 0) return PA_ERR_ARG;
-    if (batch == 0) return PA_OK;
-    if (batch > kMaxDecodeBatch) return PA_ERR_UNSUPPORTED;
+    if (batch == 0) return PA_OK;          // nothing to do; the caller returns
+    if (batch > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_ARG;
     if (!std::isfinite(scale)) return PA_ERR_ARG;
-    DecodeArgs a;
+    a = DecodeArgs{};
     a.out = out;
     a.q = q;
     a.k_cache = static_cast<const char*>(k_cache);
@@ -450,14 +594,58 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype, c
         a.max_partitions = 1;
         a.split = 0;
     }
-    hipError_t e = hipSuccess;
-    const int kind = cache_kind(cache_dtype);
-    if (kind == kBF16 && head_dim == 128) e = launch_decode<kBF16, 128>(a, stream);
-    else if (kind == kBF16 && head_dim == 64) e = launch_decode<kBF16, 64>(a, stream);
-    else if (kind == kFP8 && head_dim == 128) e = launch_decode<kFP8, 128>(a, stream);
-    else if (kind == kFP8 && head_dim == 64) e = launch_decode<kFP8, 64>(a, stream);
-    else if (kind == kF32 && head_dim == 128) e = launch_decode<kF32, 128>(a, stream);
-    else if (kind == kF32 && head_dim == 64) e = launch_decode<kF32, 64>(a, stream);
-    else return PA_ERR_UNSUPPORTED;
-    return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype, const void* k_cache,
+                                 const void* v_cache, pa_dtype_t cache_dtype, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, float scale,
+                                 int32_t partition_size, int32_t max_partitions, float* part_max,
+                                 float* part_sum, float* part_out, hipStream_t stream) {
+    DecodeArgs a;
+    pa_status_t st = pack_decode(a, out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                 v_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                                 num_heads, num_kv_heads, head_dim, block_size, scale,
+                                 partition_size, max_partitions, part_max, part_sum, part_out);
+    if (st != PA_OK || batch == 0) return st;
+    return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
+                      stream);
+}
+
+extern "C" pa_status_t pa_decode_cascade(
+    const void* q, pa_dtype_t q_dtype, const void* k_cache, const void* v_cache,
+    pa_dtype_t cache_dtype, const float* k_scale, const float* v_scale,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t batch, const int32_t* group_start, const int32_t* group_seqs,
+    const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_size,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    int32_t partition_size, int32_t max_partitions, float* part_max, float* part_sum,
+    float* part_out, hipStream_t stream) {
+    if (partition_size <= 0) return PA_ERR_ARG;
+    DecodeArgs a;
+    pa_status_t st = pack_decode(a, nullptr, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                 v_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                                 num_heads, num_kv_heads, head_dim, block_size, scale,
+                                 partition_size, max_partitions, part_max, part_sum, part_out);
+    if (st != PA_OK) return st;
+    if (num_groups < 0 || max_group_size < 0 || max_group_size > 0xFFFF) return PA_ERR_ARG;
+    if (num_groups > 0 && (!group_start || !group_seqs || !group_prefix_lens)) return PA_ERR_ARG;
+    if ((long)batch + num_groups > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+    if (batch == 0) return PA_OK;
+    a.group_start = group_start;
+    a.group_seqs = group_seqs;
+    a.group_prefix_lens = group_prefix_lens;
+    a.num_groups = num_groups;
+    const int mpc = 16 / (num_heads / num_kv_heads);
+    const long chunks = (max_group_size + mpc - 1) / mpc;
+    const long rows_bound = (long)batch + (long)num_groups * chunks;
+    return run_decode(a, cache_dtype, head_dim, rows_bound * num_kv_heads * max_partitions,
+                      stream);
 }

@@ -99,6 +99,14 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
 }
 
+// Load through the constant address space: for memory the kernel never
+// writes (block tables, scales, group lists).  A wave-uniform address then
+// becomes a scalar load, whose completion is tracked apart from the K/V
+// vector loads still in flight.
+template <class T> __device__ __forceinline__ T load_invariant(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- 16-byte global loads (non-temporal for streamed KV) --------------------

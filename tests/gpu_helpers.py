@@ -5,7 +5,8 @@ import numpy as np
 import torch
 
 from oracle import paged_attention as opa
-from paged_kv_cache_234_amd import KVPool, pa_decode, pa_decode_splitk_reduce, pa_prefill_chunk
+from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_cascade, pa_decode_splitk_reduce,
+                                    pa_prefill_chunk)
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 3e-2}
 POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
@@ -101,3 +102,37 @@ def max_abs_err(got, want):
     got = np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), "non-finite output"
     return float(np.max(np.abs(got - want))) if got.size else 0.0
+
+
+def group_arrays(w, extra_empty_groups=0, device="cuda"):
+    """group_start / group_seqs / group_prefix_lens for the workload's prefix
+    groups (prefix = the shared blocks' positions); optionally followed by
+    groups without members."""
+    start, seqs, plens = [0], [], []
+    for members, nshared in w.prefix_groups:
+        seqs.extend(int(b) for b in members)
+        start.append(len(seqs))
+        plens.append(int(nshared) * w.block_size)
+    for _ in range(extra_empty_groups):
+        start.append(len(seqs))
+        plens.append(64)
+    mg = max([len(m) for m, _ in w.prefix_groups] + [0])
+    seqs = seqs or [0]            # never read when no group has members
+    return i32(start, device), i32(seqs, device), i32(plens, device), mg
+
+
+def run_cascade(w, pool, partition_size, extra_empty_groups=0, device="cuda"):
+    """pa_decode_cascade + pa_decode_splitk_reduce; returns (out, (pm, ps, po))."""
+    q = w.q.to(device).contiguous()
+    bt, lens = i32(w.block_tables, device), i32(w.context_lens, device)
+    pmax = max(1, -(-int(np.max(w.context_lens)) // partition_size))
+    B, hq, d = q.shape
+    pm = torch.full((B, hq, pmax), float("nan"), device=device)
+    ps = torch.full((B, hq, pmax), float("nan"), device=device)
+    po = torch.full((B, hq, pmax, d), float("nan"), device=device)
+    gs, gq, gp, mg = group_arrays(w, extra_empty_groups, device)
+    pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, gs, gq, gp, mg, partition_size, pmax,
+                      pm, ps, po, pool.k_scale, pool.v_scale)
+    out = torch.empty_like(q)
+    pa_decode_splitk_reduce(out, pm, ps, po, lens, partition_size)
+    return out, (pm, ps, po)

@@ -97,3 +97,20 @@ def test_append_reduce_prefill_validation():
                                 None, 8, 2, 128, 16, 0.1, None) == _lib.PA_OK
     assert lib.pa_prefill_chunk(None, None, 1, None, 2, 64, None, None, 1, None, None, None, 4,
                                 None, 8, 2, 128, 16, 0.1, None) == _lib.PA_ERR_ARG
+
+
+def test_cascade_validation():
+    lib = _lib.load()
+
+    def call(ps=256, pmax=4, B=4, ng=1, mgs=4, gs=FAKE, gq=FAKE, gp=FAKE, parts=FAKE):
+        return lib.pa_decode_cascade(FAKE, 1, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B, gs,
+                                     gq, gp, ng, mgs, 8, 2, 128, 16, 0.1, ps, pmax, parts, parts,
+                                     parts, None)
+
+    assert call(ps=0) == _lib.PA_ERR_ARG                         # split-K only
+    assert call(parts=None) == _lib.PA_ERR_ARG                   # partial buffers required
+    assert call(gs=None) == _lib.PA_ERR_ARG                      # group arrays required
+    assert call(ng=-1) == _lib.PA_ERR_ARG
+    assert call(mgs=-1) == _lib.PA_ERR_ARG
+    assert call(B=4000, ng=200) == _lib.PA_ERR_UNSUPPORTED       # more than 4096 rows
+    assert call(B=0) == _lib.PA_OK

@@ -1,0 +1,121 @@
+"""pa_decode_cascade (shared-prefix split-K decode) parity with the fp64 oracle.
+
+A cascade computes exactly the partials pa_decode computes; only the reads
+differ (a group's shared partitions are read once for up to 16/G members).
+So the oracle here is the plain decode oracle, and the partials are compared
+with oracle_partitions partition by partition.  Cases cover every group size
+regime (16/G members per MFMA column tile: 16, 4, 2, 1 and a ragged 5 for
+G = 3), prefixes that are not a whole number of partitions, members whose
+whole context is the prefix, single-member and empty groups, sequences in no
+group and L = 0 sequences, on NaN-poisoned pools.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged_attention as opa
+from tests.gpu_helpers import (TOL, as_f64, gpu_pool, host, max_abs_err, oracle_pool,
+                               run_cascade, run_decode)
+from workloads import build_workload, make_config
+
+pytestmark = pytest.mark.gpu
+
+# members' lengths cover: exactly the prefix (no tail), one past it, ragged tails
+LENS = [128, 129, 200, 300, 140, 1000, 0, 77, 50, 64, 330, 5, 48, 96, 700, 129]
+GROUPS = [([0, 1, 2, 3, 4, 5, 15], 8),     # 128 shared positions
+          ([7, 8], 3),                     # 48: less than one 64-partition
+          ([10], 20),                      # a group of one
+          ([12, 13], 3)]                   # member 12 is all prefix (48)
+
+
+def _case(q_dtype, cache, hq, hkv, d, seed, lens=LENS, groups=GROUPS):
+    return build_workload("c", seed=seed, device="cuda", q_dtype=q_dtype, cache_dtype=cache,
+                          num_heads=hq, num_kv_heads=hkv, head_dim=d, decode_lens=lens,
+                          prefix_groups=groups)
+
+
+def _check(w, ps, extra_empty_groups=0):
+    pool = gpu_pool(w)
+    out, (pm, psum, po) = run_cascade(w, pool, ps, extra_empty_groups)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                            w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size)
+    tol = TOL[w.cache_dtype]
+    assert max_abs_err(as_f64(out), ref) <= tol
+    pmax = pm.shape[2]
+    m, l, o = opa.oracle_partitions(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                                    w.context_lens, w.scale, ps, pmax, w.k_scale, w.v_scale)
+    valid = ~np.isnan(m)
+    gm, gl, go = as_f64(pm), as_f64(psum), as_f64(po)
+    assert np.all(np.isnan(gm[~valid]))          # nothing past ceil(L / PS) is written
+    assert np.max(np.abs(gm[valid] - m[valid])) <= tol
+    assert np.max(np.abs(gl[valid] / l[valid] - 1)) <= 4 * tol
+    assert np.max(np.abs(go[valid] - o[valid])) <= tol
+    return pool, out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4)])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_cascade_matches_oracle_all_group_sizes(cache, hq, hkv, d):
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = _case(q_dtype, cache, hq, hkv, d, seed=hq * 17 + hkv + d)
+    _check(w, 64)
+
+
+@pytest.mark.parametrize("ps", [16, 32, 128, 256])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_cascade_partition_sizes(cache, ps):
+    w = _case("bf16", cache, 8, 2, 128, seed=ps + 3)
+    _check(w, ps)
+
+
+def test_cascade_with_empty_groups():
+    w = _case("bf16", "bf16", 8, 2, 128, seed=9)
+    _check(w, 64, extra_empty_groups=3)
+
+
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_cascade_without_groups_is_pa_decode_bit_exact(cache):
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = _case(q_dtype, cache, 8, 2, 128, seed=4, groups=[])
+    pool = gpu_pool(w)
+    out_c, parts_c = run_cascade(w, pool, 64)
+    out_d, parts_d = run_decode(w, pool, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_d)
+    for a, b in zip(parts_c, parts_d):
+        assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_cascade_agrees_with_pa_decode(cache):
+    w = _case("bf16", cache, 8, 2, 128, seed=12)
+    pool = gpu_pool(w)
+    out_c, _ = run_cascade(w, pool, 64)
+    out_d, _ = run_decode(w, pool, 64)
+    torch.cuda.synchronize()
+    assert max_abs_err(as_f64(out_c), as_f64(out_d)) <= TOL[cache]
+
+
+def test_cascade_full_size_prefix_shared_config():
+    """Llama-3-8B-shaped prefix-shared decode at full size (batch 256, groups
+    of 8 sharing 16 blocks), partition 256: the oracle on a sample of
+    sequences (every group's first and last member and the longest), pa_decode
+    on all of them."""
+    w = make_config(3, device="cuda")
+    pool = gpu_pool(w)
+    out_c, _ = run_cascade(w, pool, 256)
+    out_d, _ = run_decode(w, pool, 256)
+    torch.cuda.synchronize()
+    tol = TOL[w.cache_dtype]
+    assert max_abs_err(as_f64(out_c), as_f64(out_d)) <= tol
+    seqs = sorted({int(m[0]) for m, _ in w.prefix_groups[::4]} |
+                  {int(m[-1]) for m, _ in w.prefix_groups[::4]} |
+                  {int(np.argmax(w.context_lens))})
+    kp, vp = oracle_pool(w, seqs=seqs)
+    ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                            w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size, seqs=seqs)
+    assert max_abs_err(as_f64(out_c)[seqs], ref[seqs]) <= tol
