@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", default=None, choices=["spec-verify"],
+                    help="instead of a numbered config: the draft-verification step "
+                         "(pa_decode_multi over U[2, 8] causal query tokens per sequence)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cascade", action="store_true",
@@ -61,15 +64,22 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_cascade,
+    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_cascade, pa_decode_multi,
                                         pa_decode_splitk_reduce, pa_prefill_chunk, pa_selftest)
-    from workloads import make_config
+    from workloads import make_config, make_spec_verify
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
     pa_selftest()
-    w = make_config(args.config, seed=args.seed, device=dev)
-    ps = DEFAULT_PS[args.config] if args.partition_size is None else args.partition_size
+    spec = args.workload == "spec-verify"
+    if spec:
+        w = make_spec_verify(device=dev) if args.seed is None else make_spec_verify(args.seed, dev)
+        ps = 256 if args.partition_size is None else args.partition_size
+        if ps <= 0:
+            raise SystemExit("the draft-verification step is split-K only (--partition-size > 0)")
+    else:
+        w = make_config(args.config, seed=args.seed, device=dev)
+        ps = DEFAULT_PS[args.config] if args.partition_size is None else args.partition_size
 
     def i32(a):
         return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
@@ -85,10 +95,23 @@ def main():
         pools.append(p)
     new_k, new_v = w.new_k.contiguous(), w.new_v.contiguous()
     new_slots = i32(w.new_slots)
-    q = w.q.contiguous()
+    if spec:
+        # the query tokens are the rows of the workload's chunks
+        q = w.q_prefill.contiguous()
+        lens, bt = i32(w.chunk_context_lens), i32(w.chunk_block_tables)
+        qsl = i32(w.query_start_loc)
+        max_q = int(np.max(np.diff(w.query_start_loc)))
+        tok_lens = []
+        for c in range(w.num_chunks):
+            n = int(w.query_start_loc[c + 1] - w.query_start_loc[c])
+            tok_lens.extend(int(w.chunk_context_lens[c]) - n + i + 1 for i in range(n))
+        tok_lens = i32(tok_lens)
+        pmax = max(1, -(-int(np.max(w.chunk_context_lens)) // ps))
+    else:
+        q = w.q.contiguous()
+        lens, bt = i32(w.context_lens), i32(w.block_tables)
+        pmax = w.max_partitions(ps)
     B, hq, d = q.shape
-    lens, bt = i32(w.context_lens), i32(w.block_tables)
-    pmax = w.max_partitions(ps)
     part_max = torch.empty((B, hq, pmax), device=dev)
     part_sum = torch.empty((B, hq, pmax), device=dev)
     part_out = torch.empty((B, hq, pmax, d), device=dev)
@@ -103,7 +126,7 @@ def main():
             g_plens.append(int(nshared) * w.block_size)
         g_start, g_seqs, g_plens = i32(g_start), i32(g_seqs), i32(g_plens)
         g_max = max(len(m) for m, _ in w.prefix_groups)
-    has_prefill = w.num_chunks > 0
+    has_prefill = w.num_chunks > 0 and not spec
     if has_prefill:
         qp = w.q_prefill.contiguous()
         outp = torch.empty_like(qp)
@@ -124,7 +147,9 @@ def main():
         decode_only(layer)
         if ev is not None:
             ev[2].record(stream)
-        if ps > 0:
+        if spec:
+            pa_decode_splitk_reduce(out, part_max, part_sum, part_out, tok_lens, ps)
+        elif ps > 0:
             pa_decode_splitk_reduce(out, part_max, part_sum, part_out, lens, ps)
         if ev is not None:
             ev[3].record(stream)
@@ -136,7 +161,10 @@ def main():
 
     def decode_only(layer):
         pool = pools[layer % R]
-        if cascade:
+        if spec:
+            pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
+                            part_sum, part_out, pool.k_scale, pool.v_scale)
+        elif cascade:
             pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, g_start, g_seqs, g_plens, g_max,
                               ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale)
         elif ps > 0:
@@ -212,8 +240,8 @@ def main():
                for j, n in enumerate(names)}
 
     # ---- accounting -----------------------------------------------------------
-    kv_logical = w.decode_kv_bytes_logical()
-    kv_unique = w.decode_kv_bytes_unique()
+    kv_logical = w.prefill_kv_bytes() if spec else w.decode_kv_bytes_logical()
+    kv_unique = w.prefill_kv_bytes() if spec else w.decode_kv_bytes_unique()
     step_bytes = kv_logical + (w.prefill_kv_bytes() if has_prefill else 0)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_unique / (decode_ms * 1e-3) / 1e9
@@ -246,12 +274,15 @@ def main():
         "dtype": w.cache_dtype if w.cache_dtype != "fp8" else "fp8-e4m3 KV, bf16 Q",
         "data": "synthetic (seeded; no dataset, no weights)",
         "config": {
-            "workload": w.name, "seed": w.seed, "batch": w.batch, "num_heads": w.num_heads,
-            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-            "context_tokens": int(w.context_lens.sum()), "new_tokens": int(len(w.new_slots)),
+            "workload": w.name, "seed": w.seed, "batch": w.num_chunks if spec else w.batch,
+            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "context_tokens": int((w.chunk_context_lens if spec else w.context_lens).sum()),
+            "new_tokens": int(len(w.new_slots)),
             "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
             "pool_blocks": w.num_blocks, "layer_copies": R,
-            "decode_entry": "pa_decode_cascade" if cascade else "pa_decode",
+            "decode_entry": ("pa_decode_multi" if spec else
+                             "pa_decode_cascade" if cascade else "pa_decode"),
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 3),
         "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),
@@ -277,7 +308,7 @@ def main():
         result["prefill_tflops"] = round(w.prefill_flops() / (pf_ms * 1e-3) / 1e12, 2)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, ms_per_step)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, ms_per_step, kv_logical)
     print(json.dumps(result), flush=True)
 
 
@@ -313,9 +344,10 @@ def measured_traffic(workload, ps):
     return None
 
 
-def cpu_baseline(w, budget_s, gpu_ms):
+def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
-    decode sequences; scaled to the metric's unit (KV GB/s)."""
+    decode sequences (or, for a workload of chunks only, its chunks); scaled
+    to the metric's unit (KV GB/s)."""
     from oracle import paged_attention as opa
     import torch
     try:
@@ -328,29 +360,38 @@ def cpu_baseline(w, budget_s, gpu_ms):
         t = t.detach().cpu().contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
+    chunks_only = w.batch == 0
+    n_units = w.num_chunks if chunks_only else w.batch
+    lens_of = w.chunk_context_lens if chunks_only else w.context_lens
+    tables_of = w.chunk_block_tables if chunks_only else w.block_tables
     rng = np.random.default_rng(0)
-    order = rng.permutation(w.batch)
+    order = rng.permutation(n_units)
     st = opa.STORAGE_DTYPES[w.cache_dtype]
     shape_k, shape_v = opa.pool_shapes(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
                                        w.block_size)
     kp = np.zeros(shape_k, st)
     vp = np.zeros(shape_v, st)
-    qh = raw(w.q)
+    qh = raw(w.q_prefill if chunks_only else w.q)
     done, tokens, elapsed = [], 0, 0.0
     for b in order:
-        n = -(-int(w.context_lens[b]) // w.block_size)
-        blocks = w.block_tables[b, :n].astype(np.int64)
+        n = -(-int(lens_of[b]) // w.block_size)
+        blocks = tables_of[b, :n].astype(np.int64)
         sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
         idx = torch.as_tensor(sel, device=w.fill_k.device)
         kp, vp = opa.oracle_append(kp, vp, raw(w.fill_k[idx]), raw(w.fill_v[idx]),
                                    w.fill_slots[sel], w.in_dtype, w.cache_dtype, w.k_scale,
                                    w.v_scale, w.block_size)
         t = time.perf_counter()
-        opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables, w.context_lens,
-                          w.scale, w.k_scale, w.v_scale, w.block_size, seqs=[int(b)])
+        if chunks_only:
+            opa.oracle_prefill(qh, w.q_dtype, w.query_start_loc, kp, vp, w.cache_dtype,
+                               w.chunk_block_tables, w.chunk_context_lens, w.scale, w.k_scale,
+                               w.v_scale, w.block_size, chunks=[int(b)])
+        else:
+            opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables, w.context_lens,
+                              w.scale, w.k_scale, w.v_scale, w.block_size, seqs=[int(b)])
         elapsed += time.perf_counter() - t
         done.append(int(b))
-        tokens += int(w.context_lens[b])
+        tokens += int(lens_of[b])
         if elapsed >= budget_s:
             break
     kv = tokens * w.kv_bytes_per_token()
@@ -359,11 +400,14 @@ def cpu_baseline(w, budget_s, gpu_ms):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": "fp64 oracle decode of %d of %d sequences (%d context tokens, %.1f s), "
-                  "host affinity %d cores" % (len(done), w.batch, tokens, elapsed,
+        "sample": "fp64 oracle %s of %d of %d %s (%d context tokens, %.1f s), "
+                  "host affinity %d cores" % ("causal chunks" if chunks_only else "decode",
+                                              len(done), n_units,
+                                              "sequences' query tokens" if chunks_only else
+                                              "sequences", tokens, elapsed,
                                               len(os.sched_getaffinity(0))),
         "seconds": round(elapsed, 3),
-        "gpu_over_cpu": round((w.decode_kv_bytes_logical() / (gpu_ms * 1e-3)) / (kv / elapsed), 1)
+        "gpu_over_cpu": round((gpu_bytes / (gpu_ms * 1e-3)) / (kv / elapsed), 1)
         if elapsed > 0 else None,
     }
 

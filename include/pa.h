@@ -176,6 +176,41 @@ pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
                               hipStream_t stream);
 
 /*
+ * Multi-query split-K decode: several new query tokens per sequence, causal
+ * among themselves, as when a batch of draft tokens is verified in one step
+ * (infer-lab, technique table, speculative decoding row: draft proposal
+ * and one verification pass of the target; llm-infer, "What It Does":
+ * prompt-lookup speculative decoding; RustInfer, configuration options:
+ * multi-token-prediction draft tokens).  Sequence b's q_b = query_start_loc[b+1] - query_start_loc[b]
+ * tokens are rows query_start_loc[b] .. +q_b-1 of q, at positions
+ * L_b - q_b .. L_b - 1; the token at position P sees positions 0 .. P.
+ * Their K/V must already be appended.  Each (K/V tile, KV head) is read once
+ * for up to 16 / G of a sequence's query tokens.
+ *   q                  [query_start_loc[batch]][num_heads][head_dim]
+ *   part_*             [query_start_loc[batch]][num_heads][max_partitions]
+ *                      (+ [head_dim]): per query token, as pa_decode writes
+ *                      them for a context of P + 1 positions; partitions at or
+ *                      past ceil((P + 1) / partition_size) are not written.
+ *                      Merge with pa_decode_splitk_reduce over
+ *                      batch = query_start_loc[batch] rows whose context
+ *                      lengths are the tokens' P + 1.
+ *   max_query_len      host bound on q_b, <= 64 (PA_ERR_UNSUPPORTED beyond;
+ *                      longer chunks are prefill: pa_prefill_chunk)
+ * Requires partition_size > 0 and q_b <= L_b.
+ */
+pa_status_t pa_decode_multi(const void* q, pa_dtype_t q_dtype,
+                            const int32_t* query_start_loc, int32_t max_query_len,
+                            const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale,
+                            int32_t partition_size, int32_t max_partitions,
+                            float* part_max, float* part_sum, float* part_out,
+                            hipStream_t stream);
+
+/*
  * Merge split-K partials (the layout pa_decode writes) into out
  * [batch][num_heads][head_dim] of out_dtype (F32 or BF16):
  *   M = max_p m_p,  w_p = l_p * exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p

@@ -20,7 +20,8 @@ PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 EXPORTED = (
-    "pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_splitk_reduce", "pa_prefill_chunk",
+    "pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_multi", "pa_decode_splitk_reduce",
+    "pa_prefill_chunk",
     "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest",
 )
 
@@ -48,6 +49,8 @@ def load(path=LIB_PATH):
                               f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
+    lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
+                                    i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_splitk_reduce.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, st]
     lib.pa_prefill_chunk.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                                      i32, i32, i32, i32, f32, st]
@@ -56,8 +59,8 @@ def load(path=LIB_PATH):
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_selftest.argtypes = []
-    for fn in ("pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_splitk_reduce",
-               "pa_prefill_chunk", "pa_selftest"):
+    for fn in ("pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_multi",
+               "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_selftest"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +202,33 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, gr
                                   int(partition_size), int(max_partitions), _ptr(part_max),
                                   _ptr(part_sum), _ptr(part_out), _stream(stream))
     _check("pa_decode_cascade", st)
+
+
+def pa_decode_multi(q, query_start_loc, max_query_len, k_cache, v_cache, block_tables,
+                    context_lens, scale, partition_size, max_partitions, part_max, part_sum,
+                    part_out, k_scale=None, v_scale=None, stream=None):
+    """Split-K partials for q_b causal query tokens per sequence: q [T, Hq, D]
+    with T = query_start_loc[-1]; partials [T, Hq, max_partitions] (+ [D])."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    T, hq = q.shape[0], q.shape[1]
+    B = context_lens.numel()
+    if q.shape[2] != d or block_tables.shape[0] != B or query_start_loc.numel() != B + 1:
+        raise ValueError("inconsistent multi-query decode shapes")
+    if partition_size <= 0:
+        raise ValueError("pa_decode_multi needs partition_size > 0")
+    want = (T, hq, max_partitions)
+    for t in (part_max, part_sum):
+        if t is None or tuple(t.shape) != want or t.dtype != torch.float32:
+            raise ValueError("part_max/part_sum must be float32 %s" % (want,))
+    if part_out is None or tuple(part_out.shape) != want + (d,):
+        raise ValueError("part_out must be float32 %s" % (want + (d,),))
+    st = load().pa_decode_multi(_ptr(q), _dt(q), _i32(query_start_loc, "query_start_loc"),
+                                int(max_query_len), _ptr(k_cache), _ptr(v_cache), _dt(k_cache),
+                                _ptr(k_scale), _ptr(v_scale), _i32(block_tables, "block_tables"),
+                                block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,
+                                hkv, d, bs, float(scale), int(partition_size), int(max_partitions),
+                                _ptr(part_max), _ptr(part_sum), _ptr(part_out), _stream(stream))
+    _check("pa_decode_multi", st)
 
 
 def pa_decode_splitk_reduce(out, part_max, part_sum, part_out, context_lens, partition_size,

@@ -37,6 +37,7 @@
 namespace pa {
 
 constexpr int kMaxDecodeRows = 4096;
+constexpr int kMaxMultiQuery = 64;     // query tokens per sequence in pa_decode_multi
 
 struct DecodeArgs {
     void* out;
@@ -57,6 +58,10 @@ struct DecodeArgs {
     const int32_t* group_seqs;
     const int32_t* group_prefix_lens;
     int num_groups;
+    // multi-query rows: sequence b's query tokens are rows
+    // query_start_loc[b] .. query_start_loc[b+1]-1 of q and of the partials,
+    // at positions L_b - q_len_b .. L_b - 1 (causal among themselves)
+    const int32_t* query_start_loc;
     int max_blocks_per_seq;
     int batch;
     int num_heads;
@@ -103,15 +108,22 @@ void decode_kernel(DecodeArgs a) {
     const int PS = a.partition_size;
     const int tpi = (PS + TT - 1) / TT;                  // tiles of a full item
     const int Hkv = a.num_kv_heads;
-    const int mpc = 16 / a.group;                        // group members per 16 columns
+    const int mpc = 16 / a.group;                        // members / query positions per 16 columns
+    const bool multi = a.query_start_loc != nullptr;
 
     // ---- row table in LDS -------------------------------------------------------
     // Group descriptors are read together with the context lengths, and a
     // group's member list in batches of 8 independent loads, so the prologue
     // costs two dependent memory round trips.
     for (int r = tid; r < B; r += NT) {
-        s_len[r] = a.context_lens[r];
+        const int L = a.context_lens[r];
+        s_len[r] = L;
         s_aux[r] = 0;
+        if (multi) {            // (first query row << 8) | queries (<= L, < 256)
+            const int q0 = a.query_start_loc[r];
+            const int nq = max(0, min(min(a.query_start_loc[r + 1] - q0, L), 255));
+            s_aux[r] = (q0 << 8) | nq;
+        }
     }
     if (a.num_groups > 0) {
         constexpr int kBatch = 8;
@@ -142,11 +154,11 @@ void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    auto row_skip = [&](int r) { return r < B ? s_aux[r] : 0; };
+    auto row_skip = [&](int r) { return (r < B && !multi) ? s_aux[r] : 0; };
     auto row_heads = [&](int r) {
-        if (r < B) return Hkv;
-        const int members = s_aux[r] & 0xFFFF;
-        return Hkv * ((members + mpc - 1) / mpc);
+        if (r < B && !multi) return Hkv;
+        const int cols = r < B ? (s_aux[r] & 0xFF) : (s_aux[r] & 0xFFFF);
+        return Hkv * ((cols + mpc - 1) / mpc);
     };
     auto row_items = [&](int r) {
         const int L = s_len[r];
@@ -250,7 +262,7 @@ void decode_kernel(DecodeArgs a) {
     // p (partition part = p + skip), tile jj of the item; the item covers
     // positions [tb, te) in nti tiles; t0 is its first tile's global number.
     struct Cursor {
-        int r, vh, h, ch, nh, p, part, jj, n, tb, te, nti;
+        int r, vh, h, ch, nh, p, part, jj, n, tb, te, nti, qmin;
         long t0;
     };
     auto set_item = [&](Cursor& c, int r, int vh, int p, long t0) {
@@ -266,6 +278,7 @@ void decode_kernel(DecodeArgs a) {
         c.tb = c.part * PS;
         c.te = min(s_len[r], c.tb + PS);
         c.nti = (c.te - c.tb + TT - 1) / TT;
+        c.qmin = (multi && r < B) ? s_len[r] - (s_aux[r] & 0xFF) : 0x3FFFFFFF;   // first query position
         c.t0 = t0;
     };
     // only called while another tile of this wavefront's run exists
@@ -308,12 +321,23 @@ void decode_kernel(DecodeArgs a) {
     WaveSoftmax<KIND, D> st;
     typename Ops::Q qop[1];
     float c = a.scale_log2;
-    int col_seq = -1, col_hq = 0;  // this lane's column: sequence and query head (-1: none)
+    // this lane's column: row of q / the partials (-1: none), query head, and
+    // the last position it may see (multi-query rows; others see everything)
+    int col_seq = -1, col_hq = 0, col_last = 0x3FFFFFFF;
     // Q operand, column map and score multiplier of item `it`
-    auto q_for = [&](const Cursor& it, typename Ops::Q& qd, int& cs, int& chq, float& cf) {
+    auto q_for = [&](const Cursor& it, typename Ops::Q& qd, int& cs, int& chq, int& cl, float& cf) {
         cs = -1;
         chq = 0;
-        if (it.r < B) {
+        cl = 0x3FFFFFFF;
+        if (it.r < B && multi) {
+            const int aux = __builtin_amdgcn_readfirstlane(s_aux[it.r]);
+            const int i = it.ch * mpc + g / a.group;
+            if (g < mpc * a.group && i < (aux & 0xFF)) {
+                cs = (aux >> 8) + i;
+                chq = it.h * a.group + g % a.group;
+                cl = it.qmin + i;
+            }
+        } else if (it.r < B) {
             if (g < a.group) {
                 cs = it.r;
                 chq = it.h * a.group + g;
@@ -351,14 +375,15 @@ void decode_kernel(DecodeArgs a) {
     // item: those loads are complete before that tile is multiplied, so the
     // prefetched operand is complete when the compute cursor takes it.
     typename Ops::Q qnext;
-    int next_seq = -1, next_hq = 0, next_ord = -1;
+    int next_seq = -1, next_hq = 0, next_last = 0, next_ord = -1;
     float next_c = 0.f;
     int load_ord = 0, comp_ord = 0;
 
     // write an item's result from st: a split-K partial, or the output rows
     auto finish_item = [&](const Cursor& it) {
         const float lt = sum_over_groups(st.l[0]);          // against the reference mr
-        if (col_seq >= 0) {
+        // a multi-query column that sees none of the item writes nothing
+        if (col_seq >= 0 && col_last >= it.tb) {
             const float vs = (KIND == kFP8) ? load_invariant(a.v_scale + it.h) : 1.0f;
             const float inv = vs / lt;
             if (a.split) {
@@ -422,7 +447,7 @@ void decode_kernel(DecodeArgs a) {
                 if (lc.r != orow || lc.vh != ovh) {
                     ++load_ord;
                     if (next_ord <= comp_ord) {
-                        q_for(lc, qnext, next_seq, next_hq, next_c);
+                        q_for(lc, qnext, next_seq, next_hq, next_last, next_c);
                         next_ord = load_ord;
                     }
                 }
@@ -432,9 +457,10 @@ void decode_kernel(DecodeArgs a) {
         int ncomputed = 0;
         bool piece_from_start = cc.jj == 0;
         auto compute = [&](typename Ops::Regs& r) {
-            const int nvalid = cc.te - (cc.tb + cc.jj * TT);
-            const int nolimit[1] = {TT};
-            st.step(r, qop, c, nvalid, nolimit, nvalid < TT, lane);
+            const int t0 = cc.tb + cc.jj * TT;
+            const int nvalid = cc.te - t0;
+            const int limit[1] = {min(col_last - t0, TT)};
+            st.step(r, qop, c, nvalid, limit, nvalid < TT || t0 + TT - 1 > cc.qmin, lane);
             ++ncomputed;
             const bool item_done = cc.jj + 1 == cc.nti;
             const bool run_done = ncomputed == ntiles;
@@ -457,9 +483,10 @@ void decode_kernel(DecodeArgs a) {
                             qop[0] = qnext;
                             col_seq = next_seq;
                             col_hq = next_hq;
+                            col_last = next_last;
                             c = next_c;
                         } else {
-                            q_for(cc, qop[0], col_seq, col_hq, c);
+                            q_for(cc, qop[0], col_seq, col_hq, col_last, c);
                         }
                     }
                 }
@@ -469,7 +496,7 @@ void decode_kernel(DecodeArgs a) {
         };
 
         st.init();
-        q_for(cc, qop[0], col_seq, col_hq, c);
+        q_for(cc, qop[0], col_seq, col_hq, col_last, c);
         fetch_ids();
         typename Ops::Regs ra, rb;
         issue(ra);
@@ -647,5 +674,31 @@ extern "C" pa_status_t pa_decode_cascade(
     const long chunks = (max_group_size + mpc - 1) / mpc;
     const long rows_bound = (long)batch + (long)num_groups * chunks;
     return run_decode(a, cache_dtype, head_dim, rows_bound * num_kv_heads * max_partitions,
+                      stream);
+}
+
+extern "C" pa_status_t pa_decode_multi(
+    const void* q, pa_dtype_t q_dtype, const int32_t* query_start_loc, int32_t max_query_len,
+    const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, float scale, int32_t partition_size,
+    int32_t max_partitions, float* part_max, float* part_sum, float* part_out,
+    hipStream_t stream) {
+    if (partition_size <= 0) return PA_ERR_ARG;
+    DecodeArgs a;
+    pa_status_t st = pack_decode(a, nullptr, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                 v_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                                 num_heads, num_kv_heads, head_dim, block_size, scale,
+                                 partition_size, max_partitions, part_max, part_sum, part_out);
+    if (st != PA_OK) return st;
+    if (max_query_len < 0) return PA_ERR_ARG;
+    if (max_query_len > kMaxMultiQuery) return PA_ERR_UNSUPPORTED;
+    if (batch == 0 || max_query_len == 0) return PA_OK;
+    if (!query_start_loc) return PA_ERR_ARG;
+    a.query_start_loc = query_start_loc;
+    const int mpc = 16 / (num_heads / num_kv_heads);
+    const long chunks = (max_query_len + mpc - 1) / mpc;
+    return run_decode(a, cache_dtype, head_dim, (long)batch * chunks * num_kv_heads * max_partitions,
                       stream);
 }

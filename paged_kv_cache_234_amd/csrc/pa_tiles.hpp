@@ -361,8 +361,11 @@ template <int KIND, int D, int NC = 1> struct WaveSoftmax {
             m[n] = fmaxf(m[n], tmax);
             const bool bump = tmax > mr[n] + kRescaleSlack;     // true for the first finite max
             if (__builtin_amdgcn_ballot_w64(bump)) {
+                // columns that keep their reference scale by exactly 1 (a
+                // column that has seen nothing yet keeps mr = -inf, where
+                // exp2(mr - mr) would be NaN); a first finite max scales by 0
                 const float mr_new = bump ? m[n] : mr[n];
-                const float alpha = fast_exp2(mr[n] - mr_new);  // 1 where unchanged, 0 from -inf
+                const float alpha = bump ? fast_exp2(mr[n] - mr_new) : 1.0f;
                 mr[n] = mr_new;
                 l[n] *= alpha;
 #pragma unroll

@@ -114,3 +114,19 @@ def test_cascade_validation():
     assert call(mgs=-1) == _lib.PA_ERR_ARG
     assert call(B=4000, ng=200) == _lib.PA_ERR_UNSUPPORTED       # more than 4096 rows
     assert call(B=0) == _lib.PA_OK
+
+
+def test_multi_query_validation():
+    lib = _lib.load()
+
+    def call(ps=64, pmax=4, B=4, mq=8, qsl=FAKE, parts=FAKE):
+        return lib.pa_decode_multi(FAKE, 1, qsl, mq, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B,
+                                   8, 2, 128, 16, 0.1, ps, pmax, parts, parts, parts, None)
+
+    assert call(ps=0) == _lib.PA_ERR_ARG
+    assert call(parts=None) == _lib.PA_ERR_ARG
+    assert call(qsl=None) == _lib.PA_ERR_ARG
+    assert call(mq=-1) == _lib.PA_ERR_ARG
+    assert call(mq=65) == _lib.PA_ERR_UNSUPPORTED
+    assert call(mq=0) == _lib.PA_OK
+    assert call(B=0) == _lib.PA_OK

@@ -1,0 +1,111 @@
+"""pa_decode_multi (several causal query tokens per sequence, as in draft
+verification) parity with the fp64 oracle.
+
+The oracle is the prefill-chunk oracle: a sequence's q query tokens at
+positions L - q .. L - 1 form one causal chunk over its cached prefix.  The
+split-K partials of every query token are also compared with the decode
+oracle's partitions for a context of that token's position + 1.  Cases cover
+one to 64 query tokens (one and several 16-column chunks per KV head), a
+prefix of zero, contexts that end on and off tile and partition boundaries,
+every GQA regime (16 / G query tokens per 16 MFMA columns) and all three cache
+types on NaN-poisoned pools.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import paged_attention as opa
+from tests.gpu_helpers import (TOL, as_f64, gpu_pool, host, max_abs_err, oracle_pool, run_decode,
+                               run_multi, token_lens)
+from workloads import build_workload, make_spec_verify
+
+pytestmark = pytest.mark.gpu
+
+# (cached positions, query tokens)
+CHUNKS = [(0, 2), (1, 3), (14, 2), (15, 8), (16, 5), (31, 1), (62, 4), (100, 7), (127, 8),
+          (255, 6), (256, 2), (700, 8), (1000, 3)]
+
+
+def _case(cache, hq, hkv, d, chunks, seed):
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    return build_workload("mq", seed=seed, device="cuda", q_dtype=q_dtype, cache_dtype=cache,
+                          num_heads=hq, num_kv_heads=hkv, head_dim=d, prefill_chunks=chunks)
+
+
+def _check(w, ps):
+    pool = gpu_pool(w)
+    out, (pm, psum, po), tl = run_multi(w, pool, ps)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    ref = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
+                             w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens, w.scale,
+                             w.k_scale, w.v_scale, w.block_size)
+    tol = TOL[w.cache_dtype]
+    assert max_abs_err(as_f64(out), ref) <= tol
+    # every query token's partials == the decode oracle's for its own context
+    chunk_of = np.repeat(np.arange(w.num_chunks), np.diff(w.query_start_loc))
+    m, l, o = opa.oracle_partitions(host(w.q_prefill), w.q_dtype, kp, vp, w.cache_dtype,
+                                    w.chunk_block_tables[chunk_of], tl, w.scale, ps, pm.shape[2],
+                                    w.k_scale, w.v_scale)
+    valid = ~np.isnan(m)
+    gm, gl, go = as_f64(pm), as_f64(psum), as_f64(po)
+    assert np.all(np.isnan(gm[~valid]))          # nothing past ceil((P + 1) / PS) is written
+    assert np.max(np.abs(gm[valid] - m[valid])) <= tol
+    assert np.max(np.abs(gl[valid] / l[valid] - 1)) <= 4 * tol
+    assert np.max(np.abs(go[valid] - o[valid])) <= tol
+    return pool, out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4)])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_multi_query_matches_oracle_all_group_sizes(cache, hq, hkv, d):
+    w = _case(cache, hq, hkv, d, CHUNKS, seed=hq * 13 + hkv + d)
+    _check(w, 64)
+
+
+@pytest.mark.parametrize("ps", [16, 32, 256])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_multi_query_partition_sizes(cache, ps):
+    w = _case(cache, 8, 2, 128, CHUNKS, seed=ps)
+    _check(w, ps)
+
+
+def test_multi_query_up_to_64_tokens():
+    """Several 16-column chunks of query tokens per KV head (G = 4: four
+    tokens per chunk, so 64 tokens are 16 chunks)."""
+    w = _case("bf16", 32, 8, 128, [(0, 64), (5, 64), (300, 33), (64, 17)], seed=77)
+    _check(w, 64)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_last_query_token_equals_single_token_decode(cache):
+    """The last query token of each sequence sees the whole context: it is
+    ordinary decode of that sequence."""
+    w = _case(cache, 16, 2, 128, CHUNKS, seed=31)
+    pool = gpu_pool(w)
+    out, _, _ = run_multi(w, pool, 64)
+    last = w.query_start_loc[1:] - 1
+    dec, _ = run_decode(w, pool, 64, q=w.q_prefill[torch.as_tensor(last, device="cuda")],
+                        block_tables=w.chunk_block_tables, context_lens=w.chunk_context_lens)
+    torch.cuda.synchronize()
+    assert max_abs_err(as_f64(out)[last], as_f64(dec)) <= TOL[cache]
+
+
+def test_spec_verify_workload_full_size():
+    """The draft-verification workload (64 sequences, U[256, 4096] cached
+    positions, U[2, 8] drafts, Qwen2.5-3B decode shape) at full size: the
+    oracle on every eighth sequence."""
+    w = make_spec_verify(device="cuda")
+    pool = gpu_pool(w)
+    out, _, _ = run_multi(w, pool, 256)
+    torch.cuda.synchronize()
+    chunks = list(range(0, w.num_chunks, 8))
+    kp, vp = oracle_pool(w, chunks=chunks)
+    ref = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
+                             w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens, w.scale,
+                             w.k_scale, w.v_scale, w.block_size, chunks=chunks)
+    rows = np.concatenate([np.arange(w.query_start_loc[c], w.query_start_loc[c + 1])
+                           for c in chunks])
+    assert max_abs_err(as_f64(out)[rows], ref[rows]) <= TOL[w.cache_dtype]

@@ -5,4 +5,5 @@ draws sequence lengths, block assignments, slot mappings and Q/K/V values; it
 contains none of the attention arithmetic and imports neither side.
 """
 
-from .configs import Workload, build_workload, make_config, CONFIG_NAMES  # noqa: F401
+from .configs import (Workload, build_workload, make_config, make_spec_verify,  # noqa: F401
+                      CONFIG_NAMES, SPEC_VERIFY_NAME)

@@ -332,3 +332,21 @@ def make_config(index, seed=None, device="cpu"):
                               num_heads=32, num_kv_heads=8, head_dim=128, decode_lens=lens,
                               prefill_chunks=[(int(p), 512) for p in prefix], rng=rng)
     raise KeyError(index)
+
+
+SPEC_VERIFY_NAME = "qwen2.5-3b-bf16-spec-verify-b64"
+
+
+def make_spec_verify(seed=6, device="cpu"):
+    """Draft verification step on the Qwen2.5-3B decode shape (16 query / 2 KV
+    heads, head_dim 128, bf16): 64 sequences with U[256, 4096] cached
+    positions, each checking U[2, 8] draft tokens whose K/V are appended in
+    this step (causal among themselves)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cached = rng.integers(256, 4096, size=64, endpoint=True)
+    drafts = rng.integers(2, 8, size=64, endpoint=True)
+    return build_workload(SPEC_VERIFY_NAME, seed=seed, device=device, num_heads=16,
+                          num_kv_heads=2, head_dim=128,
+                          prefill_chunks=[(int(p), int(k)) for p, k in zip(cached, drafts)],
+                          rng=rng)
+
