@@ -133,6 +133,199 @@ void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged prefill for bf16 and fp8 caches.
+//
+// The register-streaming kernel above loads every K/V tile once per
+// wavefront, so at 32 query rows per wavefront the bytes it pulls from L2
+// per MFMA are several times what L2 can feed.  Here the four wavefronts of
+// a workgroup work on the same (chunk, KV head) and share each 64-position
+// K/V tile through LDS: wavefront w loads block w of the tile (its physical
+// id is wave-uniform, a scalar load), widens fp8 to bf16 on the way, and
+// writes it in the layouts the bf16 MFMA operands read as one contiguous
+// 1 KB per wave-wide 16-byte LDS read:
+//   K  [block][D/8][16 tokens][8 dims]            (the bf16 pool layout)
+//   V  [half][D/16][key run q][16 dims][8 keys]   (half = 32 positions; run q
+//                                                  = keys 8q .. 8q+7)
+// Each wavefront then runs NC 16-column query tiles over the tile, two
+// 32-position halves through the bf16 tile operations.  Tiles are double
+// buffered: the next tile's global loads are in flight during the multiply,
+// and one barrier per tile orders the LDS writes against the reads.
+// ---------------------------------------------------------------------------
+constexpr int kLdsTile = 64;                  // positions per staged tile (4 blocks)
+constexpr int kLdsCols = 2;                   // 16-column query tiles per wavefront
+
+template <int KIND, int D, int NC>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_lds_kernel(PrefillArgs a) {
+    using Ops = TileOps<kBF16, D>;            // staged operands are bf16 for both caches
+    using QT = uint16_t;
+    constexpr int NW = 4, NS = Ops::NS, NVT = Ops::NVT;
+    constexpr int KB = kBlock * D * 2;        // one block's K (or V) in bf16
+    constexpr int ELEM = KIND == kFP8 ? 1 : 2;
+    constexpr int NLD = KIND == kFP8 ? D / 64 : D / 32;     // 16-byte loads per lane for K (and V)
+    __shared__ __align__(16) char s_k[2][4 * KB];
+    __shared__ __align__(16) char s_v[2][4 * KB];
+
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int tg = item % a.wg_per_head;
+    const int h = (item / a.wg_per_head) % a.num_kv_heads;
+    const int c = item / (a.wg_per_head * a.num_kv_heads);
+
+    const int q0 = a.query_start_loc[c];
+    const int C = a.query_start_loc[c + 1] - q0;
+    const int L = a.context_lens[c];
+    const int P = L - C;
+    const int npos = a.npos;
+    const int wg_rows = NW * NC * npos;
+    const int wg_row0 = tg * wg_rows;
+    if (wg_row0 >= C || P < 0) return;                   // the whole workgroup leaves together
+    const int kend = P + min(C, wg_row0 + wg_rows);      // keys [0, kend) are touched
+    const int ntiles = (kend + kLdsTile - 1) / kLdsTile;
+    const int last_blk = (kend - 1) / kBlock;
+
+    // this wavefront's query columns
+    const int row0 = wg_row0 + wave * NC * npos;
+    const int wrows = max(0, min(NC * npos, C - row0));
+    const int g = lane & 15, grp = lane >> 4;
+    const int pi = g / a.group, gh = g % a.group;
+    typename Ops::Q qop[NC];
+    int my_last[NC];
+    bool col_valid[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int r = n * npos + pi;
+        col_valid[n] = pi < npos && r < wrows;
+        const QT* qrow = reinterpret_cast<const QT*>(a.q) +
+                         ((long)(q0 + row0 + (col_valid[n] ? r : 0)) * a.num_heads + h * a.group + gh) * D;
+        Ops::load_q(qop[n], qrow, col_valid[n], lane);
+        my_last[n] = P + row0 + (col_valid[n] ? r : 0);
+    }
+    const int w_kend = P + row0 + wrows;                 // keys this wavefront needs
+    const int min_last = P + row0;
+    float cs = a.scale_log2;
+    if (KIND == kFP8) cs *= load_invariant(a.k_scale + h);
+
+    const int32_t* bt = a.block_tables + (long)c * a.max_blocks_per_seq;
+    const long head_stride = (long)kBlock * D * ELEM;
+    const long blk_stride = head_stride * a.num_kv_heads;
+    const char* kbase = a.k_cache + h * head_stride;
+    const char* vbase = a.v_cache + h * head_stride;
+
+    // ---- staging: wavefront w moves block w of tile t --------------------------
+    u32x4 sk[NLD], sv[NLD];
+    auto stage_load = [&](int t) {
+        const int lb = min(t * 4 + wave, last_blk);
+        const long phys = load_invariant(bt + __builtin_amdgcn_readfirstlane(lb));
+        const char* kb = kbase + phys * blk_stride;
+        const char* vb = vbase + phys * blk_stride;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            sk[u] = load16(kb + 16 * (lane + kWave * u));
+            sv[u] = load16(vb + 16 * (lane + kWave * u));
+        }
+    };
+    auto stage_store = [&](int buf) {
+        char* kd = s_k[buf] + wave * KB;
+        char* vd = s_v[buf] + (wave >> 1) * (2 * KB);
+        const int run0 = (wave & 1) * 2;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int piece = lane + kWave * u;
+            if (KIND == kFP8) {
+                // K piece = (16-dim chunk c16, token): two bf16 chunks (2 c16, 2 c16 + 1)
+                const int c16 = piece >> 4, tok = piece & 15;
+                const bf16x8 lo = fp8x8_to_bf16x8(sk[u][0], sk[u][1]);
+                const bf16x8 hi = fp8x8_to_bf16x8(sk[u][2], sk[u][3]);
+                *reinterpret_cast<bf16x8*>(kd + ((2 * c16) * 16 + tok) * 16) = lo;
+                *reinterpret_cast<bf16x8*>(kd + ((2 * c16 + 1) * 16 + tok) * 16) = hi;
+                // V piece = dim d, 16 tokens: runs run0 (tokens 0-7) and run0 + 1 (8-15)
+                const int d = piece;
+                const bf16x8 v0 = fp8x8_to_bf16x8(sv[u][0], sv[u][1]);
+                const bf16x8 v1 = fp8x8_to_bf16x8(sv[u][2], sv[u][3]);
+                const int t16 = d >> 4, dd = d & 15;
+                *reinterpret_cast<bf16x8*>(vd + ((t16 * 4 + run0) * 16 + dd) * 16) = v0;
+                *reinterpret_cast<bf16x8*>(vd + ((t16 * 4 + run0 + 1) * 16 + dd) * 16) = v1;
+            } else {
+                // K: same layout as the pool; V piece = half of dim d's 32 bytes
+                *reinterpret_cast<u32x4*>(kd + 16 * piece) = sk[u];
+                const int d = piece >> 1, half = piece & 1;
+                const int t16 = d >> 4, dd = d & 15;
+                *reinterpret_cast<u32x4*>(vd + ((t16 * 4 + run0 + half) * 16 + dd) * 16) = sv[u];
+            }
+        }
+    };
+
+    WaveSoftmax<kBF16, D, NC> st;
+    st.init();
+    auto compute = [&](int buf, int t) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int t0 = t * kLdsTile + hh * 32;
+            if (t0 >= w_kend) continue;
+            typename Ops::Regs r;
+            const char* ks = s_k[buf] + 2 * hh * KB;
+            const char* vs = s_v[buf] + hh * (2 * KB);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int k = 0; k < NS; ++k)
+                    r.k[i][k] = *reinterpret_cast<const u32x4*>(ks + i * KB + ((4 * k + grp) * 16 + g) * 16);
+#pragma unroll
+            for (int v = 0; v < NVT; ++v)
+                r.v[v] = *reinterpret_cast<const u32x4*>(vs + ((v * 4 + grp) * 16 + g) * 16);
+            const int nvalid = min(kend - t0, 32);
+            const bool masked = (t0 + 31 > min_last) || (nvalid < 32);
+            int limit[NC];
+#pragma unroll
+            for (int n = 0; n < NC; ++n) limit[n] = my_last[n] - t0;
+            st.step(r, qop, cs, nvalid, limit, masked, lane);
+        }
+    };
+
+    stage_load(0);
+    stage_store(0);
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) stage_load(t + 1);
+        __syncthreads();                       // tile t is in LDS; tile t-1's readers are done
+        if (wrows > 0) compute(buf, t);
+        if (t + 1 < ntiles) stage_store(buf ^ 1);
+    }
+
+    const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const float l = sum_over_groups(st.l[n]);        // against the reference mr
+        if (!col_valid[n]) continue;
+        const float inv = vsc / l;
+        const long orow =
+            ((long)(q0 + row0 + n * npos + pi) * a.num_heads + h * a.group + gh) * D;
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int d = 16 * t + 4 * grp;
+            const f32x4 v = st.o[n][t] * inv;
+            u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + d) = pk;
+        }
+    }
+}
+
+template <int KIND, int D, int NC>
+static hipError_t launch_prefill_lds(PrefillArgs a, int num_chunks, int max_query_len,
+                                     hipStream_t stream) {
+    const int rows = 4 * NC * a.npos;
+    a.wg_per_head = (max_query_len + rows - 1) / rows;
+    const long grid = (long)num_chunks * a.num_kv_heads * a.wg_per_head;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_lds_kernel<KIND, D, NC>), dim3((unsigned)grid), dim3(4 * kWave),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
 template <int KIND, int D>
 static hipError_t launch_prefill(PrefillArgs a, int num_chunks, int max_query_len,
                                  hipStream_t stream) {
@@ -188,10 +381,10 @@ extern "C" pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_d
     a.scale_log2 = scale * kLog2e;
     hipError_t e;
     const int kind = cache_kind(cache_dtype);
-    if (kind == kBF16 && head_dim == 128) e = launch_prefill<kBF16, 128>(a, num_chunks, max_query_len, stream);
-    else if (kind == kBF16 && head_dim == 64) e = launch_prefill<kBF16, 64>(a, num_chunks, max_query_len, stream);
-    else if (kind == kFP8 && head_dim == 128) e = launch_prefill<kFP8, 128>(a, num_chunks, max_query_len, stream);
-    else if (kind == kFP8 && head_dim == 64) e = launch_prefill<kFP8, 64>(a, num_chunks, max_query_len, stream);
+    if (kind == kBF16 && head_dim == 128) e = launch_prefill_lds<kBF16, 128, kLdsCols>(a, num_chunks, max_query_len, stream);
+    else if (kind == kBF16 && head_dim == 64) e = launch_prefill_lds<kBF16, 64, kLdsCols>(a, num_chunks, max_query_len, stream);
+    else if (kind == kFP8 && head_dim == 128) e = launch_prefill_lds<kFP8, 128, kLdsCols>(a, num_chunks, max_query_len, stream);
+    else if (kind == kFP8 && head_dim == 64) e = launch_prefill_lds<kFP8, 64, kLdsCols>(a, num_chunks, max_query_len, stream);
     else if (kind == kF32 && head_dim == 128) e = launch_prefill<kF32, 128>(a, num_chunks, max_query_len, stream);
     else if (kind == kF32 && head_dim == 64) e = launch_prefill<kF32, 64>(a, num_chunks, max_query_len, stream);
     else return PA_ERR_UNSUPPORTED;
