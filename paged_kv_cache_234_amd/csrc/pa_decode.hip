@@ -78,12 +78,16 @@ template <> struct QType<kF32> { using T = float; };
 
 // Online-softmax state of one wavefront's piece of an item, parked in LDS
 // until the wavefront owning the item's first tile merges it.
-template <int NVT> struct SegSlot {
-    f32x4 o[NVT][kWave];
-    float m[kWave], mr[kWave], l[kWave];
+template <int NVT, int NC> struct SegSlot {
+    f32x4 o[NC][NVT][kWave];
+    float m[NC][kWave], mr[NC][kWave], l[NC][kWave];
 };
 
-template <int KIND, int D, int NW>
+// NC: 16-column query tiles per wavefront.  Sequence rows use one (their
+// columns are one KV head's G <= 16 query heads); group and multi-query rows
+// give each virtual head NC * 16 columns, so one K/V tile feeds up to
+// NC * 16 / G members or query positions.
+template <int KIND, int D, int NW, int NC>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
     using Ops = TileOps<KIND, D>;
@@ -98,7 +102,7 @@ void decode_kernel(DecodeArgs a) {
     __shared__ int s_aux[kMaxDecodeRows];
     __shared__ int s_tpre[kMaxDecodeRows + 1];
     __shared__ int s_wsum[NW];
-    __shared__ SegSlot<NVT> s_seg[NW];           // each wave's first piece, if cut
+    __shared__ SegSlot<NVT, NC> s_seg[NW];       // each wave's first piece, if cut
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -109,6 +113,7 @@ void decode_kernel(DecodeArgs a) {
     const int tpi = (PS + TT - 1) / TT;                  // tiles of a full item
     const int Hkv = a.num_kv_heads;
     const int mpc = 16 / a.group;                        // members / query positions per 16 columns
+    const int mpv = mpc * NC;                            // ... per virtual head
     const bool multi = a.query_start_loc != nullptr;
 
     // ---- row table in LDS -------------------------------------------------------
@@ -158,7 +163,7 @@ void decode_kernel(DecodeArgs a) {
     auto row_heads = [&](int r) {
         if (r < B && !multi) return Hkv;
         const int cols = r < B ? (s_aux[r] & 0xFF) : (s_aux[r] & 0xFFFF);
-        return Hkv * ((cols + mpc - 1) / mpc);
+        return Hkv * ((cols + mpv - 1) / mpv);
     };
     auto row_items = [&](int r) {
         const int L = s_len[r];
@@ -318,49 +323,64 @@ void decode_kernel(DecodeArgs a) {
     bool tail_open = false;       // this wave's last piece ends inside its item
     Cursor tail_item;
 
-    WaveSoftmax<KIND, D> st;
-    typename Ops::Q qop[1];
+    WaveSoftmax<KIND, D, NC> st;
+    typename Ops::Q qop[NC];
     float c = a.scale_log2;
-    // this lane's column: row of q / the partials (-1: none), query head, and
-    // the last position it may see (multi-query rows; others see everything)
-    int col_seq = -1, col_hq = 0, col_last = 0x3FFFFFFF;
-    // Q operand, column map and score multiplier of item `it`
-    auto q_for = [&](const Cursor& it, typename Ops::Q& qd, int& cs, int& chq, int& cl, float& cf) {
-        cs = -1;
-        chq = 0;
-        cl = 0x3FFFFFFF;
+    // this lane's column in query tile n: row of q / the partials (-1: none),
+    // query head, and the last position it may see (multi-query rows; others
+    // see everything)
+    int col_seq[NC], col_hq[NC], col_last[NC];
+    // Q operands, column map and score multiplier of item `it`
+    auto q_for = [&](const Cursor& it, typename Ops::Q (&qd)[NC], int (&cs)[NC], int (&chq)[NC],
+                     int (&cl)[NC], float& cf) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            cs[n] = -1;
+            chq[n] = 0;
+            cl[n] = 0x3FFFFFFF;
+        }
         if (it.r < B && multi) {
             const int aux = __builtin_amdgcn_readfirstlane(s_aux[it.r]);
-            const int i = it.ch * mpc + g / a.group;
-            if (g < mpc * a.group && i < (aux & 0xFF)) {
-                cs = (aux >> 8) + i;
-                chq = it.h * a.group + g % a.group;
-                cl = it.qmin + i;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const int i = it.ch * mpv + n * mpc + g / a.group;
+                if (g < mpc * a.group && i < (aux & 0xFF)) {
+                    cs[n] = (aux >> 8) + i;
+                    chq[n] = it.h * a.group + g % a.group;
+                    cl[n] = it.qmin + i;
+                }
             }
         } else if (it.r < B) {
             if (g < a.group) {
-                cs = it.r;
-                chq = it.h * a.group + g;
+                cs[0] = it.r;
+                chq[0] = it.h * a.group + g;
             }
         } else {
             // this chunk's members, read with scalar loads (no wait on the
             // K/V loads in flight) and handed to their lanes by select
             const int aux = __builtin_amdgcn_readfirstlane(s_aux[it.r]);
-            const int first = (aux >> 16) + it.ch * mpc;
-            const int cnt = min(mpc, (aux & 0xFFFF) - it.ch * mpc);
-            const int m = g / a.group;
-            int sq = -1;
-            for (int k = 0; k < cnt; ++k) {
-                const int v = load_invariant(a.group_seqs + first + k);
-                sq = (m == k) ? v : sq;
-            }
-            if (g < mpc * a.group && sq >= 0 && sq < B) {
-                cs = sq;
-                chq = it.h * a.group + g % a.group;
+            const int first = (aux >> 16) + it.ch * mpv;
+            const int cnt = min(mpv, (aux & 0xFFFF) - it.ch * mpv);
+#pragma unroll
+            for (int n = 0; n < NC; ++n) {
+                const int m = n * mpc + g / a.group;
+                int sq = -1;
+                for (int k = n * mpc; k < min(cnt, (n + 1) * mpc); ++k) {
+                    const int v = load_invariant(a.group_seqs + first + k);
+                    sq = (m == k) ? v : sq;
+                }
+                if (g < mpc * a.group && sq >= 0 && sq < B) {
+                    cs[n] = sq;
+                    chq[n] = it.h * a.group + g % a.group;
+                }
             }
         }
-        const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((long)max(cs, 0) * a.num_heads + chq) * D;
-        Ops::load_q(qd, qrow, cs >= 0, lane);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const QT* qrow = reinterpret_cast<const QT*>(a.q) +
+                             ((long)max(cs[n], 0) * a.num_heads + chq[n]) * D;
+            Ops::load_q(qd[n], qrow, cs[n] >= 0, lane);
+        }
         cf = a.scale_log2;
         if (KIND == kFP8) cf *= load_invariant(a.k_scale + it.h);
     };
@@ -374,33 +394,38 @@ void decode_kernel(DecodeArgs a) {
     // The prefetch is issued before the K/V loads of the tile ahead of the
     // item: those loads are complete before that tile is multiplied, so the
     // prefetched operand is complete when the compute cursor takes it.
-    typename Ops::Q qnext;
-    int next_seq = -1, next_hq = 0, next_last = 0, next_ord = -1;
+    // (one query tile only: two would not fit beside two tiles of K/V)
+    constexpr bool kPrefetchQ = NC == 1;
+    typename Ops::Q qnext[NC];
+    int next_seq[NC], next_hq[NC], next_last[NC], next_ord = -1;
     float next_c = 0.f;
     int load_ord = 0, comp_ord = 0;
 
     // write an item's result from st: a split-K partial, or the output rows
     auto finish_item = [&](const Cursor& it) {
-        const float lt = sum_over_groups(st.l[0]);          // against the reference mr
-        // a multi-query column that sees none of the item writes nothing
-        if (col_seq >= 0 && col_last >= it.tb) {
-            const float vs = (KIND == kFP8) ? load_invariant(a.v_scale + it.h) : 1.0f;
+        const float vs = (KIND == kFP8) ? load_invariant(a.v_scale + it.h) : 1.0f;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const float lt = sum_over_groups(st.l[n]);      // against the reference mr
+            // a multi-query column that sees none of the item writes nothing
+            if (col_seq[n] < 0 || col_last[n] < it.tb) continue;
             const float inv = vs / lt;
             if (a.split) {
-                const long pi = ((long)col_seq * a.num_heads + col_hq) * a.max_partitions + it.part;
+                const long pi =
+                    ((long)col_seq[n] * a.num_heads + col_hq[n]) * a.max_partitions + it.part;
                 float* po = a.part_out + pi * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t)
-                    *reinterpret_cast<f32x4*>(po + 16 * t + 4 * grp) = st.o[0][t] * inv;
+                    *reinterpret_cast<f32x4*>(po + 16 * t + 4 * grp) = st.o[n][t] * inv;
                 if (grp == 0) {
-                    a.part_max[pi] = st.m[0] * kLn2;
-                    a.part_sum[pi] = lt * fast_exp2(st.mr[0] - st.m[0]);   // against the true max
+                    a.part_max[pi] = st.m[n] * kLn2;
+                    a.part_sum[pi] = lt * fast_exp2(st.mr[n] - st.m[n]);   // against the true max
                 }
             } else {
-                const long oi = ((long)col_seq * a.num_heads + col_hq) * D;
+                const long oi = ((long)col_seq[n] * a.num_heads + col_hq[n]) * D;
 #pragma unroll
                 for (int t = 0; t < NVT; ++t) {
-                    const f32x4 v = st.o[0][t] * inv;
+                    const f32x4 v = st.o[n][t] * inv;
                     const int d = 16 * t + 4 * grp;
                     if (KIND == kF32) {
                         *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi + d) = v;
@@ -412,12 +437,15 @@ void decode_kernel(DecodeArgs a) {
             }
         }
     };
-    auto park = [&](SegSlot<NVT>& s) {
+    auto park = [&](SegSlot<NVT, NC>& s) {
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) s.o[t][lane] = st.o[0][t];
-        s.m[lane] = st.m[0];
-        s.mr[lane] = st.mr[0];
-        s.l[lane] = st.l[0];
+        for (int n = 0; n < NC; ++n) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) s.o[n][t][lane] = st.o[n][t];
+            s.m[n][lane] = st.m[n];
+            s.mr[n][lane] = st.mr[n];
+            s.l[n][lane] = st.l[n];
+        }
     };
 
     if (ntiles > 0) {
@@ -444,7 +472,7 @@ void decode_kernel(DecodeArgs a) {
                 if (lc.r != orow)
                     bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
                 fetch_ids();
-                if (lc.r != orow || lc.vh != ovh) {
+                if (kPrefetchQ && (lc.r != orow || lc.vh != ovh)) {
                     ++load_ord;
                     if (next_ord <= comp_ord) {
                         q_for(lc, qnext, next_seq, next_hq, next_last, next_c);
@@ -459,7 +487,9 @@ void decode_kernel(DecodeArgs a) {
         auto compute = [&](typename Ops::Regs& r) {
             const int t0 = cc.tb + cc.jj * TT;
             const int nvalid = cc.te - t0;
-            const int limit[1] = {min(col_last - t0, TT)};
+            int limit[NC];
+#pragma unroll
+            for (int n = 0; n < NC; ++n) limit[n] = min(col_last[n] - t0, TT);
             st.step(r, qop, c, nvalid, limit, nvalid < TT || t0 + TT - 1 > cc.qmin, lane);
             ++ncomputed;
             const bool item_done = cc.jj + 1 == cc.nti;
@@ -479,14 +509,17 @@ void decode_kernel(DecodeArgs a) {
                     piece_from_start = true;
                     st.init();
                     if (cc.r != orow || cc.vh != ovh) {
-                        if (++comp_ord == next_ord) {
-                            qop[0] = qnext;
-                            col_seq = next_seq;
-                            col_hq = next_hq;
-                            col_last = next_last;
+                        if (kPrefetchQ && ++comp_ord == next_ord) {
+#pragma unroll
+                            for (int n = 0; n < NC; ++n) {
+                                qop[n] = qnext[n];
+                                col_seq[n] = next_seq[n];
+                                col_hq[n] = next_hq[n];
+                                col_last[n] = next_last[n];
+                            }
                             c = next_c;
                         } else {
-                            q_for(cc, qop[0], col_seq, col_hq, col_last, c);
+                            q_for(cc, qop, col_seq, col_hq, col_last, c);
                         }
                     }
                 }
@@ -496,7 +529,7 @@ void decode_kernel(DecodeArgs a) {
         };
 
         st.init();
-        q_for(cc, qop[0], col_seq, col_hq, col_last, c);
+        q_for(cc, qop, col_seq, col_hq, col_last, c);
         fetch_ids();
         typename Ops::Regs ra, rb;
         issue(ra);
@@ -526,22 +559,25 @@ void decode_kernel(DecodeArgs a) {
             const long s0 = wave_start(w), s1 = wave_start(w + 1);
             if (s0 >= item_end) break;
             if (s1 == s0) continue;
-            const SegSlot<NVT>& s = s_seg[w];
-            const float mr2 = s.mr[lane];
-            const float mnew = fmaxf(st.mr[0], mr2);
-            const float a1 = st.mr[0] == mnew ? 1.f : fast_exp2(st.mr[0] - mnew);
-            const float a2 = mr2 == mnew ? 1.f : fast_exp2(mr2 - mnew);
-            st.mr[0] = mnew;
-            st.m[0] = fmaxf(st.m[0], s.m[lane]);
-            st.l[0] = st.l[0] * a1 + s.l[lane] * a2;
+            const SegSlot<NVT, NC>& s = s_seg[w];
 #pragma unroll
-            for (int t = 0; t < NVT; ++t) st.o[0][t] = st.o[0][t] * a1 + s.o[t][lane] * a2;
+            for (int n = 0; n < NC; ++n) {
+                const float mr2 = s.mr[n][lane];
+                const float mnew = fmaxf(st.mr[n], mr2);
+                const float a1 = st.mr[n] == mnew ? 1.f : fast_exp2(st.mr[n] - mnew);
+                const float a2 = mr2 == mnew ? 1.f : fast_exp2(mr2 - mnew);
+                st.mr[n] = mnew;
+                st.m[n] = fmaxf(st.m[n], s.m[n][lane]);
+                st.l[n] = st.l[n] * a1 + s.l[n][lane] * a2;
+#pragma unroll
+                for (int t = 0; t < NVT; ++t) st.o[n][t] = st.o[n][t] * a1 + s.o[n][t][lane] * a2;
+            }
         }
         finish_item(tail_item);
     }
 }
 
-template <int KIND, int D>
+template <int KIND, int D, int NC>
 static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
     constexpr int NW = 4;
     int dev = 0, cus = 256;
@@ -551,24 +587,29 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     long grid = (long)cus * waves_per_simd(KIND, D);
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
-    hipLaunchKernelGGL((decode_kernel<KIND, D, NW>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-// items_bound: an upper bound on (row, virtual head, partition) items
+// items_bound: an upper bound on (row, virtual head, partition) items; wide:
+// two 16-column query tiles per wavefront (group and multi-query rows)
 static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int head_dim,
-                              long items_bound, hipStream_t stream) {
+                              long items_bound, bool wide, hipStream_t stream) {
     hipError_t e = hipSuccess;
     const int kind = cache_kind(cache_dtype);
     auto tiles = [&](int tt) { return items_bound * ((a.partition_size + tt - 1) / tt); };
-    if (kind == kBF16 && head_dim == 128) e = launch_decode<kBF16, 128>(a, tiles(32), stream);
-    else if (kind == kBF16 && head_dim == 64) e = launch_decode<kBF16, 64>(a, tiles(32), stream);
-    else if (kind == kFP8 && head_dim == 128) e = launch_decode<kFP8, 128>(a, tiles(64), stream);
-    else if (kind == kFP8 && head_dim == 64) e = launch_decode<kFP8, 64>(a, tiles(64), stream);
-    else if (kind == kF32 && head_dim == 128) e = launch_decode<kF32, 128>(a, tiles(16), stream);
-    else if (kind == kF32 && head_dim == 64) e = launch_decode<kF32, 64>(a, tiles(16), stream);
+#define PA_LAUNCH(K, DD, TT)                                                          \
+    (wide ? launch_decode<K, DD, 2>(a, tiles(TT), stream)                             \
+          : launch_decode<K, DD, 1>(a, tiles(TT), stream))
+    if (kind == kBF16 && head_dim == 128) e = PA_LAUNCH(kBF16, 128, 32);
+    else if (kind == kBF16 && head_dim == 64) e = PA_LAUNCH(kBF16, 64, 32);
+    else if (kind == kFP8 && head_dim == 128) e = PA_LAUNCH(kFP8, 128, 64);
+    else if (kind == kFP8 && head_dim == 64) e = PA_LAUNCH(kFP8, 64, 64);
+    else if (kind == kF32 && head_dim == 128) e = PA_LAUNCH(kF32, 128, 16);
+    else if (kind == kF32 && head_dim == 64) e = PA_LAUNCH(kF32, 64, 16);
     else return PA_ERR_UNSUPPORTED;
+#undef PA_LAUNCH
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -643,7 +684,7 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype, c
                                  partition_size, max_partitions, part_max, part_sum, part_out);
     if (st != PA_OK || batch == 0) return st;
     return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
-                      stream);
+                      false, stream);
 }
 
 extern "C" pa_status_t pa_decode_cascade(
@@ -670,10 +711,10 @@ extern "C" pa_status_t pa_decode_cascade(
     a.group_seqs = group_seqs;
     a.group_prefix_lens = group_prefix_lens;
     a.num_groups = num_groups;
-    const int mpc = 16 / (num_heads / num_kv_heads);
-    const long chunks = (max_group_size + mpc - 1) / mpc;
+    const int mpv = 2 * (16 / (num_heads / num_kv_heads));   // members per virtual head
+    const long chunks = (max_group_size + mpv - 1) / mpv;
     const long rows_bound = (long)batch + (long)num_groups * chunks;
-    return run_decode(a, cache_dtype, head_dim, rows_bound * num_kv_heads * max_partitions,
+    return run_decode(a, cache_dtype, head_dim, rows_bound * num_kv_heads * max_partitions, true,
                       stream);
 }
 
@@ -697,8 +738,8 @@ extern "C" pa_status_t pa_decode_multi(
     if (batch == 0 || max_query_len == 0) return PA_OK;
     if (!query_start_loc) return PA_ERR_ARG;
     a.query_start_loc = query_start_loc;
-    const int mpc = 16 / (num_heads / num_kv_heads);
-    const long chunks = (max_query_len + mpc - 1) / mpc;
+    const int mpv = 2 * (16 / (num_heads / num_kv_heads));   // query tokens per virtual head
+    const long chunks = (max_query_len + mpv - 1) / mpv;
     return run_decode(a, cache_dtype, head_dim, (long)batch * chunks * num_kv_heads * max_partitions,
-                      stream);
+                      true, stream);
 }
