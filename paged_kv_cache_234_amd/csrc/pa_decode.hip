@@ -87,7 +87,9 @@ template <int NVT, int NC> struct SegSlot {
 // columns are one KV head's G <= 16 query heads); group and multi-query rows
 // give each virtual head NC * 16 columns, so one K/V tile feeds up to
 // NC * 16 / G members or query positions.
-template <int KIND, int D, int NW, int NC>
+// PLAIN: sequence rows only (pa_decode); the group and multi-query row code
+// is compiled out.
+template <int KIND, int D, int NW, int NC, bool PLAIN>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
     using Ops = TileOps<KIND, D>;
@@ -108,13 +110,13 @@ void decode_kernel(DecodeArgs a) {
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int B = a.batch;
-    const int R = B + a.num_groups;
+    const int R = PLAIN ? B : B + a.num_groups;
     const int PS = a.partition_size;
     const int tpi = (PS + TT - 1) / TT;                  // tiles of a full item
     const int Hkv = a.num_kv_heads;
     const int mpc = 16 / a.group;                        // members / query positions per 16 columns
     const int mpv = mpc * NC;                            // ... per virtual head
-    const bool multi = a.query_start_loc != nullptr;
+    const bool multi = !PLAIN && a.query_start_loc != nullptr;
 
     // ---- row table in LDS -------------------------------------------------------
     // Group descriptors are read together with the context lengths, and a
@@ -130,7 +132,7 @@ void decode_kernel(DecodeArgs a) {
             s_aux[r] = (q0 << 8) | nq;
         }
     }
-    if (a.num_groups > 0) {
+    if (!PLAIN && a.num_groups > 0) {
         constexpr int kBatch = 8;
         for (int j = tid; j < a.num_groups; j += NT) {
             const int first = min(max(a.group_start[j], 0), 0x7FFF);
@@ -159,9 +161,9 @@ void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    auto row_skip = [&](int r) { return (r < B && !multi) ? s_aux[r] : 0; };
+    auto row_skip = [&](int r) { return (!PLAIN && r < B && !multi) ? s_aux[r] : 0; };
     auto row_heads = [&](int r) {
-        if (r < B && !multi) return Hkv;
+        if (PLAIN || (r < B && !multi)) return Hkv;
         const int cols = r < B ? (s_aux[r] & 0xFF) : (s_aux[r] & 0xFFFF);
         return Hkv * ((cols + mpv - 1) / mpv);
     };
@@ -284,6 +286,10 @@ void decode_kernel(DecodeArgs a) {
         c.te = min(s_len[r], c.tb + PS);
         c.nti = (c.te - c.tb + TT - 1) / TT;
         c.qmin = (multi && r < B) ? s_len[r] - (s_aux[r] & 0xFF) : 0x3FFFFFFF;   // first query position
+        if (PLAIN) {
+            c.h = vh;
+            c.ch = 0;
+        }
         c.t0 = t0;
     };
     // only called while another tile of this wavefront's run exists
@@ -304,7 +310,7 @@ void decode_kernel(DecodeArgs a) {
     // sequence whose block table a row reads: the row's own, or its group's
     // first member's
     auto table_seq = [&](int r) {
-        if (r < B) return r;
+        if (PLAIN || r < B) return r;
         const int sq = load_invariant(a.group_seqs + __builtin_amdgcn_readfirstlane(s_aux[r] >> 16));
         return (sq >= 0 && sq < B) ? sq : 0;
     };
@@ -350,7 +356,7 @@ void decode_kernel(DecodeArgs a) {
                     cl[n] = it.qmin + i;
                 }
             }
-        } else if (it.r < B) {
+        } else if (PLAIN || it.r < B) {
             if (g < a.group) {
                 cs[0] = it.r;
                 chq[0] = it.h * a.group + g;
@@ -577,7 +583,7 @@ void decode_kernel(DecodeArgs a) {
     }
 }
 
-template <int KIND, int D, int NC>
+template <int KIND, int D, int NC, bool PLAIN>
 static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
     constexpr int NW = 4;
     int dev = 0, cus = 256;
@@ -587,7 +593,7 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     long grid = (long)cus * waves_per_simd(KIND, D);
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
-    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -600,8 +606,8 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     const int kind = cache_kind(cache_dtype);
     auto tiles = [&](int tt) { return items_bound * ((a.partition_size + tt - 1) / tt); };
 #define PA_LAUNCH(K, DD, TT)                                                          \
-    (wide ? launch_decode<K, DD, 2>(a, tiles(TT), stream)                             \
-          : launch_decode<K, DD, 1>(a, tiles(TT), stream))
+    (wide ? launch_decode<K, DD, 2, false>(a, tiles(TT), stream)                      \
+          : launch_decode<K, DD, 1, true>(a, tiles(TT), stream))
     if (kind == kBF16 && head_dim == 128) e = PA_LAUNCH(kBF16, 128, 32);
     else if (kind == kBF16 && head_dim == 64) e = PA_LAUNCH(kBF16, 64, 32);
     else if (kind == kFP8 && head_dim == 128) e = PA_LAUNCH(kFP8, 128, 64);
