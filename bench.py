@@ -44,6 +44,9 @@ def parse():
                          "(pa_decode_multi over U[2, 8] causal query tokens per sequence)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-fuse-append", action="store_true",
+                    help="append the decode tokens with pa_kv_append before pa_decode instead of "
+                         "pa_decode_append's single launch")
     ap.add_argument("--no-cascade", action="store_true",
                     help="decode prefix-sharing batches with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--eager", action="store_true",
@@ -64,8 +67,9 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_cascade, pa_decode_multi,
-                                        pa_decode_splitk_reduce, pa_prefill_chunk, pa_selftest)
+    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_append, pa_decode_cascade,
+                                        pa_decode_multi, pa_decode_splitk_reduce, pa_prefill_chunk,
+                                        pa_selftest)
     from workloads import make_config, make_spec_verify
 
     dev = "cuda:0"
@@ -127,6 +131,18 @@ def main():
         g_start, g_seqs, g_plens = i32(g_start), i32(g_seqs), i32(g_plens)
         g_max = max(len(m) for m, _ in w.prefix_groups)
     has_prefill = w.num_chunks > 0 and not spec
+    # plain decode steps append each sequence's new token inside the decode launch
+    fused = not (spec or cascade or has_prefill or args.no_fuse_append)
+    if fused:
+        rows = np.zeros(B, np.int64)
+        fslots = np.full(B, -1, np.int32)
+        j = 0
+        for b in range(B):
+            if int(w.context_lens[b]) > 0:
+                rows[b], fslots[b] = w.new_rows[j], w.new_slots[j]
+                j += 1
+        ridx = torch.as_tensor(rows, device=dev)
+        fk, fv, fslots = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous(), i32(fslots)
     if has_prefill:
         qp = w.q_prefill.contiguous()
         outp = torch.empty_like(qp)
@@ -141,10 +157,17 @@ def main():
         pool = pools[layer % R]
         if ev is not None:
             ev[0].record(stream)
-        pool.append(new_k, new_v, new_slots)
+        if not fused:
+            pool.append(new_k, new_v, new_slots)
         if ev is not None:
             ev[1].record(stream)
-        decode_only(layer)
+        if fused:
+            pa_decode_append(None if ps > 0 else out, q, fk, fv, fslots, pool.k, pool.v, bt, lens,
+                             w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
+                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
+                             part_out=part_out)
+        else:
+            decode_only(layer)
         if ev is not None:
             ev[2].record(stream)
         if spec:
@@ -235,7 +258,9 @@ def main():
     for i in range(args.steps):
         step(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
-    names = ["kv_append", "decode", "splitk_reduce", "prefill_chunk"][:nev - 1]
+    names = (["(append fused)", "decode_append"] if fused else ["kv_append", "decode"]) + \
+        ["splitk_reduce", "prefill_chunk"]
+    names = names[:nev - 1]
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                for j, n in enumerate(names)}
 
@@ -283,6 +308,13 @@ def main():
             "pool_blocks": w.num_blocks, "layer_copies": R,
             "decode_entry": ("pa_decode_multi" if spec else
                              "pa_decode_cascade" if cascade else "pa_decode"),
+            "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
+                             else "pa_decode_append" if fused
+                             else "pa_kv_append + %s%s%s" % (
+                                 "pa_decode_multi" if spec else
+                                 "pa_decode_cascade" if cascade else "pa_decode",
+                                 " + pa_decode_splitk_reduce" if ps > 0 else "",
+                                 " + pa_prefill_chunk" if has_prefill else "")),
         },
         "us_per_layer_step": round(ms_per_step * 1e3, 3),
         "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),

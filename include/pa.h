@@ -22,6 +22,8 @@
  *                            llm-infer, prefix caching).  With
  *                            partition_size > 0 it computes split-K partials
  *                            instead (flash-decoding).
+ *   pa_decode_append         pa_kv_append of each sequence's newest token
+ *                            and pa_decode in one launch.
  *   pa_decode_splitk_reduce  merge those partials into the output.
  *   pa_prefill_chunk         causal attention of prefill chunks over their
  *                            cached prefix (InferX, "Status": chunked
@@ -134,6 +136,34 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
                       int32_t partition_size, int32_t max_partitions,
                       float* part_max, float* part_sum, float* part_out,
                       hipStream_t stream);
+
+/*
+ * Append and decode in one launch: the same pool bytes and results as
+ * pa_kv_append of each sequence's newest token followed by pa_decode, for
+ * the layer-step of a decode batch (llm-infer, "What It Does": the captured
+ * per-layer decode graph writes the KV cache beside attention).  The
+ * wavefront that reads the block of position L_b - 1 for KV head h writes
+ * that token there first, so no other launch or synchronisation is needed.
+ *   k_new, v_new   [batch][num_kv_heads][head_dim] of q_dtype: sequence b's
+ *                  newest token (position L_b - 1)
+ *   new_slots      [batch] int32: that token's slot, which must be position
+ *                  L_b - 1 of b's block table, or -1 when its K/V are already
+ *                  in the pool (e.g. a token inside a prefix-shared block);
+ *                  L_b >= 1 when new_slots[b] >= 0
+ * Other arguments, outputs, layouts and errors as pa_decode; the pools are
+ * written (fp8 caches encode as pa_kv_append does).
+ */
+pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
+                             const void* k_new, const void* v_new, const int32_t* new_slots,
+                             void* k_cache, void* v_cache, pa_dtype_t cache_dtype,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t batch,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale,
+                             int32_t partition_size, int32_t max_partitions,
+                             float* part_max, float* part_sum, float* part_out,
+                             hipStream_t stream);
 
 /*
  * Shared-prefix ("cascade") split-K decode: the same partials as pa_decode

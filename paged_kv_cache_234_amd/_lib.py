@@ -20,8 +20,8 @@ PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 EXPORTED = (
-    "pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_multi", "pa_decode_splitk_reduce",
-    "pa_prefill_chunk",
+    "pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade", "pa_decode_multi",
+    "pa_decode_splitk_reduce", "pa_prefill_chunk",
     "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest",
 )
 
@@ -47,6 +47,8 @@ def load(path=LIB_PATH):
     lib.pa_kv_append.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, st]
     lib.pa_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                               f32, i32, i32, vp, vp, vp, st]
+    lib.pa_decode_append.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
+                                     i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
@@ -59,8 +61,8 @@ def load(path=LIB_PATH):
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_selftest.argtypes = []
-    for fn in ("pa_kv_append", "pa_decode", "pa_decode_cascade", "pa_decode_multi",
-               "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_selftest"):
+    for fn in ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade",
+               "pa_decode_multi", "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_selftest"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -168,6 +170,39 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_sca
                           int(partition_size), int(max_partitions), _ptr(part_max),
                           _ptr(part_sum), _ptr(part_out), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_tables,
+                     context_lens, scale, k_scale=None, v_scale=None, partition_size=0,
+                     max_partitions=1, part_max=None, part_sum=None, part_out=None, stream=None):
+    """pa_kv_append of each sequence's newest token (k_new, v_new [B, Hkv, D],
+    new_slots int32 [B], -1 to skip) and pa_decode, in one launch."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    B, hq = q.shape[0], q.shape[1]
+    if q.shape[2] != d or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent decode shapes")
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError("k_new/v_new must be [B, num_kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype or new_slots.numel() != B:
+        raise ValueError("k_new/v_new must have q's dtype; new_slots one entry per sequence")
+    if partition_size > 0:
+        want = (B, hq, max_partitions)
+        for t in (part_max, part_sum):
+            if t is None or tuple(t.shape) != want or t.dtype != torch.float32:
+                raise ValueError("part_max/part_sum must be float32 %s" % (want,))
+        if part_out is None or tuple(part_out.shape) != want + (d,):
+            raise ValueError("part_out must be float32 %s" % (want + (d,),))
+    elif out is None or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = load().pa_decode_append(_ptr(out) if partition_size == 0 else None, _ptr(q), _dt(q),
+                                 _ptr(k_new), _ptr(v_new), _i32(new_slots, "new_slots"),
+                                 _ptr(k_cache), _ptr(v_cache), _dt(k_cache), _ptr(k_scale),
+                                 _ptr(v_scale), _i32(block_tables, "block_tables"),
+                                 block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,
+                                 hkv, d, bs, float(scale), int(partition_size),
+                                 int(max_partitions), _ptr(part_max), _ptr(part_sum),
+                                 _ptr(part_out), _stream(stream))
+    _check("pa_decode_append", st)
 
 
 def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, group_start,

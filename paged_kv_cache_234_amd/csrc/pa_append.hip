@@ -5,27 +5,12 @@
 // paragraph) writes the cache as fp8 e4m3 with per-layer K/V scales frozen
 // at warm-up.  Here the scale is one fp32 value per KV head (K and V apart).
 //
-// One thread moves 8 consecutive head_dim elements of one (token, head):
-// a 16-byte (bf16) or 32-byte (fp32) read, contiguous stores into the K pool
-// (K[block][head][d / X][offset][d % X], X = 16 bytes of elements) and 8
-// element stores into the token-minor V tile (V[block][head][d][offset]).  fp8 encoding is an IEEE binary32 divide by
-// the scale, saturation to +-448 and the hardware's round-to-nearest-even
-// OCP e4m3 conversion; NaN is written as 0x7F.
+// One thread moves 8 consecutive head_dim elements of one (token, head)
+// (write_token_chunk in pa_write.hpp: layouts and fp8 encoding).
 #include "pa_internal.hpp"
+#include "pa_write.hpp"
 
 namespace pa {
-
-__device__ __forceinline__ uint32_t encode_e4m3_pair(float x0, float x1, float s) {
-    float y0 = x0 / s;                     // correctly rounded (built with
-    float y1 = x1 / s;                     // -fhip-fp32-correctly-rounded-divide-sqrt)
-    const bool n0 = y0 != y0, n1 = y1 != y1;
-    y0 = fminf(fmaxf(y0, -448.0f), 448.0f);
-    y1 = fminf(fmaxf(y1, -448.0f), 448.0f);
-    uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
-    if (n0) pk = (pk & 0xFF00u) | 0x7Fu;
-    if (n1) pk = (pk & 0x00FFu) | 0x7F00u;
-    return pk;
-}
 
 template <int IN, int CACHE, int D>
 __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_new,
@@ -37,6 +22,7 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
                                                      const int32_t* __restrict__ slots,
                                                      int num_tokens, int num_kv_heads) {
     constexpr int CH = D / 8;                         // 8-element chunks per row
+    constexpr int IB = (IN == kF32) ? 4 : 2;          // input element bytes
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long total = (long)num_tokens * num_kv_heads * CH;
     if (idx >= total) return;
@@ -45,62 +31,12 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
     const long t = idx / ((long)CH * num_kv_heads);
     const int slot = slots[t];
     if (slot < 0) return;
-    const long blk = slot / kBlock;
-    const int off = slot % kBlock;
-    const long src = (t * num_kv_heads + h) * D + 8 * c;
-    // element index of K[blk][h][d / X][off][d % X] for d = 8c (X elements per 16 bytes)
-    constexpr int X = (CACHE == kF32) ? 4 : (CACHE == kBF16 ? 8 : 16);
-    auto kidx = [&](int d) -> long {
-        return (((blk * num_kv_heads + h) * (D / X) + d / X) * kBlock + off) * X + d % X;
-    };
-    const long vdst = ((blk * num_kv_heads + h) * D + 8 * c) * kBlock + off;
-
-    if (CACHE == kF32) {
-        const float* ks = static_cast<const float*>(k_new) + src;
-        const float* vsrc = static_cast<const float*>(v_new) + src;
-        u32x4 k0 = load16_cached(ks), k1 = load16_cached(ks + 4);
-        u32x4 v0 = load16_cached(vsrc), v1 = load16_cached(vsrc + 4);
-        float* kc = reinterpret_cast<float*>(k_cache);
-        *reinterpret_cast<u32x4*>(kc + kidx(8 * c)) = k0;
-        *reinterpret_cast<u32x4*>(kc + kidx(8 * c + 4)) = k1;
-        uint32_t* vd = reinterpret_cast<uint32_t*>(v_cache) + vdst;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vd[e * kBlock] = v0[e];
-            vd[(e + 4) * kBlock] = v1[e];
-        }
-    } else if (CACHE == kBF16) {
-        u32x4 kv = load16_cached(static_cast<const uint16_t*>(k_new) + src);
-        u32x4 vv = load16_cached(static_cast<const uint16_t*>(v_new) + src);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kidx(8 * c)) = kv;
-        uint16_t* vd = reinterpret_cast<uint16_t*>(v_cache) + vdst;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vd[(2 * e) * kBlock] = (uint16_t)(vv[e] & 0xFFFFu);
-            vd[(2 * e + 1) * kBlock] = (uint16_t)(vv[e] >> 16);
-        }
-    } else {  // bf16 -> fp8 e4m3
-        const float ksc = k_scale[h], vsc = v_scale[h];
-        u32x4 kv = load16_cached(static_cast<const uint16_t*>(k_new) + src);
-        u32x4 vv = load16_cached(static_cast<const uint16_t*>(v_new) + src);
-        uint32_t kq[2], vq[2];
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            const uint32_t ka = kv[2 * w], kb = kv[2 * w + 1];
-            const uint32_t lo = encode_e4m3_pair(bf16_bits_to_f32(ka & 0xFFFF), bf16_bits_to_f32(ka >> 16), ksc);
-            const uint32_t hi = encode_e4m3_pair(bf16_bits_to_f32(kb & 0xFFFF), bf16_bits_to_f32(kb >> 16), ksc);
-            kq[w] = lo | (hi << 16);
-            const uint32_t va = vv[2 * w], vb2 = vv[2 * w + 1];
-            const uint32_t vlo = encode_e4m3_pair(bf16_bits_to_f32(va & 0xFFFF), bf16_bits_to_f32(va >> 16), vsc);
-            const uint32_t vhi = encode_e4m3_pair(bf16_bits_to_f32(vb2 & 0xFFFF), bf16_bits_to_f32(vb2 >> 16), vsc);
-            vq[w] = vlo | (vhi << 16);
-        }
-        u32x2 kk = {kq[0], kq[1]};
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(k_cache) + kidx(8 * c)) = kk;
-        uint8_t* vd = reinterpret_cast<uint8_t*>(v_cache) + vdst;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vd[e * kBlock] = (uint8_t)(vq[e >> 2] >> (8 * (e & 3)));
-    }
+    const long row = (t * num_kv_heads + h) * D * IB;
+    const float ksc = CACHE == kFP8 ? k_scale[h] : 1.0f;
+    const float vsc = CACHE == kFP8 ? v_scale[h] : 1.0f;
+    write_token_chunk<CACHE, D>(static_cast<const char*>(k_new) + row,
+                                static_cast<const char*>(v_new) + row, k_cache, v_cache,
+                                slot / kBlock, slot % kBlock, h, num_kv_heads, c, ksc, vsc);
 }
 
 template <int IN, int CACHE, int D>

@@ -33,6 +33,7 @@
 
 #include "pa_internal.hpp"
 #include "pa_tiles.hpp"
+#include "pa_write.hpp"
 
 namespace pa {
 
@@ -62,6 +63,13 @@ struct DecodeArgs {
     // query_start_loc[b] .. query_start_loc[b+1]-1 of q and of the partials,
     // at positions L_b - q_len_b .. L_b - 1 (causal among themselves)
     const int32_t* query_start_loc;
+    // fused append (plain decode): sequence b's newest token, at position
+    // L_b - 1, goes to slot new_slots[b] (-1: already in the pool)
+    const void* k_new;
+    const void* v_new;
+    const int32_t* new_slots;
+    char* k_cache_w;
+    char* v_cache_w;
     int max_blocks_per_seq;
     int batch;
     int num_heads;
@@ -260,6 +268,36 @@ void decode_kernel(DecodeArgs a) {
     auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
     const long g0 = wave_start(wave), g1 = wave_start(wave + 1);
     const int ntiles = (int)(g1 - g0);
+
+    // ---- fused append: the wavefront holding the last tile of (b, h) -- the
+    // only one that reads the block of position L_b - 1 for head h -- writes
+    // b's new token for head h there before loading anything, then fences so
+    // its own loads see it.
+    if (PLAIN && a.new_slots != nullptr && ntiles > 0) {
+        constexpr int IB = KIND == kF32 ? 4 : 2;          // input element bytes
+        const int r_first = row_of(g0), r_last = row_of(g1 - 1);
+        bool wrote = false;
+        for (int r = r_first; r <= r_last; ++r) {
+            const int th = row_head_tiles(r);
+            const int slot = load_invariant(a.new_slots + r);
+            if (th == 0 || slot < 0) continue;
+            const long base = s_tpre[r];
+            for (int h = 0; h < Hkv; ++h) {
+                const long last = base + (long)(h + 1) * th - 1;
+                if (last < g0 || last >= g1) continue;
+                const long row = ((long)r * Hkv + h) * D * IB;
+                const float ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
+                const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
+                if (lane < D / 8)
+                    write_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
+                                               static_cast<const char*>(a.v_new) + row,
+                                               a.k_cache_w, a.v_cache_w, slot / kBlock,
+                                               slot % kBlock, h, Hkv, lane, ksc, vsc);
+                wrote = true;
+            }
+        }
+        if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");    // its own later loads
+    }
 
     const int g = lane & 15, grp = lane >> 4;
     const long head_stride = (long)kBlock * D * ELEM;              // one (block, head) tile
@@ -689,6 +727,33 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype, c
                                  num_heads, num_kv_heads, head_dim, block_size, scale,
                                  partition_size, max_partitions, part_max, part_sum, part_out);
     if (st != PA_OK || batch == 0) return st;
+    return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
+                      false, stream);
+}
+
+extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
+                                        const void* k_new, const void* v_new,
+                                        const int32_t* new_slots, void* k_cache, void* v_cache,
+                                        pa_dtype_t cache_dtype, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, float scale,
+                                        int32_t partition_size, int32_t max_partitions,
+                                        float* part_max, float* part_sum, float* part_out,
+                                        hipStream_t stream) {
+    DecodeArgs a;
+    pa_status_t st = pack_decode(a, out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                 v_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                                 num_heads, num_kv_heads, head_dim, block_size, scale,
+                                 partition_size, max_partitions, part_max, part_sum, part_out);
+    if (st != PA_OK || batch == 0) return st;
+    if (!k_new || !v_new || !new_slots) return PA_ERR_ARG;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_slots = new_slots;
+    a.k_cache_w = static_cast<char*>(k_cache);
+    a.v_cache_w = static_cast<char*>(v_cache);
     return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
                       false, stream);
 }

@@ -24,13 +24,38 @@ def host(t):
     return t.numpy()
 
 
-def gpu_pool(w, device="cuda"):
-    """Poisoned pool filled with every occupied slot through pa_kv_append."""
+def gpu_pool(w, device="cuda", without_new=False):
+    """Poisoned pool filled through pa_kv_append with every occupied slot (or
+    every slot but those of this step's new decode tokens)."""
     pool = KVPool(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device=device,
                   k_scale=w.k_scale, v_scale=w.v_scale)
-    pool.append(w.fill_k.to(device).contiguous(), w.fill_v.to(device).contiguous(),
-                i32(w.fill_slots, device))
+    rows = np.arange(len(w.fill_slots))
+    if without_new:
+        new = set(int(r) for r, s in zip(w.new_rows, w.new_slots) if s >= 0)
+        rows = np.array([r for r in rows if r not in new], dtype=np.int64)
+    idx = torch.as_tensor(rows, device=w.fill_k.device)
+    pool.append(w.fill_k[idx].to(device).contiguous(), w.fill_v[idx].to(device).contiguous(),
+                i32(w.fill_slots[rows], device))
     return pool
+
+
+def decode_new_tokens(w, device="cuda"):
+    """Per decode sequence: its newest token's K/V [B, Hkv, D] and slot [B]
+    (-1 for L = 0 or when the token sits in a prefix-shared block)."""
+    B = w.batch
+    rows = np.zeros(B, np.int64)
+    slots = np.full(B, -1, np.int32)
+    j = 0
+    for b in range(B):
+        if int(w.context_lens[b]) == 0:
+            continue
+        rows[b] = w.new_rows[j]
+        slots[b] = w.new_slots[j]
+        j += 1
+    idx = torch.as_tensor(rows, device=w.fill_k.device)
+    k = w.fill_k[idx].to(device).contiguous()
+    v = w.fill_v[idx].to(device).contiguous()
+    return k, v, i32(slots, device)
 
 
 def oracle_pool(w, seqs=None, chunks=None):
