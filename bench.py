@@ -161,13 +161,7 @@ def main():
             pool.append(new_k, new_v, new_slots)
         if ev is not None:
             ev[1].record(stream)
-        if fused:
-            pa_decode_append(None if ps > 0 else out, q, fk, fv, fslots, pool.k, pool.v, bt, lens,
-                             w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
-                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
-                             part_out=part_out)
-        else:
-            decode_only(layer)
+        decode_only(layer)
         if ev is not None:
             ev[2].record(stream)
         if spec:
@@ -184,7 +178,12 @@ def main():
 
     def decode_only(layer):
         pool = pools[layer % R]
-        if spec:
+        if fused:
+            pa_decode_append(out if ps == 0 else None, q, fk, fv, fslots, pool.k, pool.v, bt, lens,
+                             w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
+                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
+                             part_out=part_out)
+        elif spec:
             pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
                             part_sum, part_out, pool.k_scale, pool.v_scale)
         elif cascade:
@@ -306,7 +305,7 @@ def main():
             "new_tokens": int(len(w.new_slots)),
             "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
             "pool_blocks": w.num_blocks, "layer_copies": R,
-            "decode_entry": ("pa_decode_multi" if spec else
+            "decode_entry": ("pa_decode_append" if fused else "pa_decode_multi" if spec else
                              "pa_decode_cascade" if cascade else "pa_decode"),
             "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
@@ -326,7 +325,8 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode",
+            "kernel": ("pa_decode_append" if fused else "pa_decode_multi" if spec else
+                       "pa_decode_cascade" if cascade else "pa_decode"),
             "duration_us": round(decode_ms * 1e3, 3),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -125,6 +125,9 @@ pa_status_t pa_kv_append(const void* k_new, const void* v_new, pa_dtype_t in_dty
  *                  and part_out [batch][num_heads][max_partitions][head_dim]
  *                  (fp32).  Partitions at or past ceil(L / PS) are not written.
  *   max_partitions >= ceil(max_b L_b / PS) (host-known bound; sizes the grid)
+ * A context length beyond max_blocks_per_seq * 16 (or, split-K, beyond
+ * max_partitions * PS) is cut there: nothing past the table row or the
+ * partial buffers is read or written.
  */
 pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
                       const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
@@ -148,8 +151,9 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
  *                  newest token (position L_b - 1)
  *   new_slots      [batch] int32: that token's slot, which must be position
  *                  L_b - 1 of b's block table, or -1 when its K/V are already
- *                  in the pool (e.g. a token inside a prefix-shared block);
- *                  L_b >= 1 when new_slots[b] >= 0
+ *                  in the pool (e.g. a token inside a prefix-shared block).
+ *                  Any other value writes nothing.
+ *                  k_new, v_new and new_slots all NULL: no append.
  * Other arguments, outputs, layouts and errors as pa_decode; the pools are
  * written (fp8 caches encode as pa_kv_append does).
  */

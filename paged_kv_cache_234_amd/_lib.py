@@ -176,15 +176,19 @@ def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_ta
                      context_lens, scale, k_scale=None, v_scale=None, partition_size=0,
                      max_partitions=1, part_max=None, part_sum=None, part_out=None, stream=None):
     """pa_kv_append of each sequence's newest token (k_new, v_new [B, Hkv, D],
-    new_slots int32 [B], -1 to skip) and pa_decode, in one launch."""
+    new_slots int32 [B], -1 to skip; all three None: no append) and
+    pa_decode, in one launch."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     B, hq = q.shape[0], q.shape[1]
     if q.shape[2] != d or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("inconsistent decode shapes")
-    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
-        raise ValueError("k_new/v_new must be [B, num_kv_heads, head_dim]")
-    if k_new.dtype != q.dtype or v_new.dtype != q.dtype or new_slots.numel() != B:
-        raise ValueError("k_new/v_new must have q's dtype; new_slots one entry per sequence")
+    if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots is None):
+        raise ValueError("k_new, v_new and new_slots go together")
+    if k_new is not None:
+        if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+            raise ValueError("k_new/v_new must be [B, num_kv_heads, head_dim]")
+        if k_new.dtype != q.dtype or v_new.dtype != q.dtype or new_slots.numel() != B:
+            raise ValueError("k_new/v_new must have q's dtype; new_slots one entry per sequence")
     if partition_size > 0:
         want = (B, hq, max_partitions)
         for t in (part_max, part_sum):
@@ -195,7 +199,8 @@ def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_ta
     elif out is None or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
     st = load().pa_decode_append(_ptr(out) if partition_size == 0 else None, _ptr(q), _dt(q),
-                                 _ptr(k_new), _ptr(v_new), _i32(new_slots, "new_slots"),
+                                 _ptr(k_new), _ptr(v_new),
+                                 None if new_slots is None else _i32(new_slots, "new_slots"),
                                  _ptr(k_cache), _ptr(v_cache), _dt(k_cache), _ptr(k_scale),
                                  _ptr(v_scale), _i32(block_tables, "block_tables"),
                                  block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,

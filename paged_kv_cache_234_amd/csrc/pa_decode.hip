@@ -131,7 +131,10 @@ void decode_kernel(DecodeArgs a) {
     // group's member list in batches of 8 independent loads, so the prologue
     // costs two dependent memory round trips.
     for (int r = tid; r < B; r += NT) {
-        const int L = a.context_lens[r];
+        // positions past the table row or the partial buffers are never read
+        const int L = (int)std::min<long>(a.context_lens[r],
+                                          std::min<long>((long)a.max_blocks_per_seq * kBlock,
+                                                         (long)a.max_partitions * PS));
         s_len[r] = L;
         s_aux[r] = 0;
         if (multi) {            // (first query row << 8) | queries (<= L, < 256)
@@ -271,20 +274,28 @@ void decode_kernel(DecodeArgs a) {
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
     // only one that reads the block of position L_b - 1 for head h -- writes
-    // b's new token for head h there before loading anything, then fences so
-    // its own loads see it.
+    // b's new token for head h there before loading anything.  A wavefront's
+    // vector memory accesses to one address are performed in order, so its
+    // later K/V loads of that block return the new token without a wait.
     if (PLAIN && a.new_slots != nullptr && ntiles > 0) {
         constexpr int IB = KIND == kF32 ? 4 : 2;          // input element bytes
         const int r_first = row_of(g0), r_last = row_of(g1 - 1);
-        bool wrote = false;
         for (int r = r_first; r <= r_last; ++r) {
             const int th = row_head_tiles(r);
-            const int slot = load_invariant(a.new_slots + r);
-            if (th == 0 || slot < 0) continue;
+            if (th == 0) continue;
             const long base = s_tpre[r];
-            for (int h = 0; h < Hkv; ++h) {
-                const long last = base + (long)(h + 1) * th - 1;
-                if (last < g0 || last >= g1) continue;
+            // first head whose last tile, base + (h + 1) * th - 1, is at or after g0
+            const long x = g0 - base + 1;
+            const int h0 = x <= 0 ? 0 : (int)std::min<long>(Hkv, (x + th - 1) / th - 1);
+            if (h0 >= Hkv || base + (long)(h0 + 1) * th - 1 >= g1) continue;
+            // only the slot the table gives position L - 1 (the block read below)
+            const int lp = max(s_len[r] - 1, 0);
+            const int slot = load_invariant(a.new_slots + r);
+            const int want = load_invariant(a.block_tables + (long)r * a.max_blocks_per_seq +
+                                            lp / kBlock) * kBlock + lp % kBlock;
+            if (slot < 0 || slot != want) continue;
+            for (int h = h0; h < Hkv; ++h) {
+                if (base + (long)(h + 1) * th - 1 >= g1) break;
                 const long row = ((long)r * Hkv + h) * D * IB;
                 const float ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
                 const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
@@ -293,10 +304,8 @@ void decode_kernel(DecodeArgs a) {
                                                static_cast<const char*>(a.v_new) + row,
                                                a.k_cache_w, a.v_cache_w, slot / kBlock,
                                                slot % kBlock, h, Hkv, lane, ksc, vsc);
-                wrote = true;
             }
         }
-        if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");    // its own later loads
     }
 
     const int g = lane & 15, grp = lane >> 4;
@@ -576,6 +585,7 @@ void decode_kernel(DecodeArgs a) {
         q_for(cc, qop, col_seq, col_hq, col_last, c);
         fetch_ids();
         typename Ops::Regs ra, rb;
+        // tile i is computed while tile i + 1 is in flight
         issue(ra);
         while (true) {
             if (nloaded < ntiles) {
@@ -748,12 +758,15 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
                                  num_heads, num_kv_heads, head_dim, block_size, scale,
                                  partition_size, max_partitions, part_max, part_sum, part_out);
     if (st != PA_OK || batch == 0) return st;
-    if (!k_new || !v_new || !new_slots) return PA_ERR_ARG;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.new_slots = new_slots;
-    a.k_cache_w = static_cast<char*>(k_cache);
-    a.v_cache_w = static_cast<char*>(v_cache);
+    const int given = (k_new != nullptr) + (v_new != nullptr) + (new_slots != nullptr);
+    if (given != 0 && given != 3) return PA_ERR_ARG;
+    if (given == 3) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.new_slots = new_slots;
+        a.k_cache_w = static_cast<char*>(k_cache);
+        a.v_cache_w = static_cast<char*>(v_cache);
+    }
     return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
                       false, stream);
 }

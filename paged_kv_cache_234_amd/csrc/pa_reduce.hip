@@ -91,6 +91,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(void* __restrict__ out,
 // Few partitions (max_partitions <= 64): one wavefront per (sequence, query
 // head), four per workgroup.  Lane p holds partition p's (m, l); the weights
 // are broadcast with v_readlane while each lane accumulates D/64 columns.
+// The first U partition rows are loaded together with (m, l), so up to U
+// partitions cost one memory round trip.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out,
                                                           const float* __restrict__ part_max,
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out
                                                           int num_heads, int partition_size,
                                                           int max_partitions, int npairs) {
     constexpr int C = D / kWave;                       // columns per lane
+    constexpr int U = 16;                              // partition rows in flight
     const int lane = lane_id();
     const int bh = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
     if (bh >= npairs) return;
@@ -107,32 +110,43 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out
     const int L = context_lens[b];
     const int P = min((L + partition_size - 1) / partition_size, max_partitions);
     const long base = (long)bh * max_partitions;
-    const float mp = lane < P ? part_max[base + lane] : -INFINITY;
-    const float M = wave_max(mp);
-    const float w = lane < P ? part_sum[base + lane] * fast_exp2((mp - M) * kLog2e) : 0.f;
-    const float W = wave_sum(w);
-    float acc[C];
-#pragma unroll
-    for (int k = 0; k < C; ++k) acc[k] = 0.f;
+    // Every load is unconditional, at an index clamped into the caller's
+    // buffer rather than into [0, P), so none waits for the context length
+    // (or for another load); values at or past P are masked by selects.
     const float* po = part_out + base * D + C * lane;
-    // eight partition rows in flight at a time
-    constexpr int U = 8;
-    for (int p0 = 0; p0 < P; p0 += U) {
-        float row[U][C];
+    auto load_rows = [&](float (&row)[U][C], int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int k = 0; k < C; ++k)
-                row[u][k] = (p0 + u < P) ? po[(long)(p0 + u) * D + k] : 0.f;
+                row[u][k] = po[(long)min(p0 + u, max_partitions - 1) * D + k];
+    };
+    const int pl = min(lane, max_partitions - 1);
+    const float m_raw = part_max[base + pl], l_raw = part_sum[base + pl];
+    float row[U][C];
+    load_rows(row, 0);
+    __builtin_amdgcn_sched_barrier(0);          // all of them out before the first wait
+    const float mp = lane < P ? m_raw : -INFINITY;
+    const float M = wave_max(mp);
+    const float w = lane < P ? l_raw * fast_exp2((mp - M) * kLog2e) : 0.f;
+    const float W = wave_sum(w);
+    float acc[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc[k] = 0.f;
+    auto accumulate = [&](const float (&row)[U][C], int p0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int pp = min(p0 + u, kWave - 1);
-            const float wp = (p0 + u < P) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                                           __builtin_bit_cast(int, w), pp))
-                                          : 0.f;
+            const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                           __builtin_bit_cast(int, w), pp));
 #pragma unroll
-            for (int k = 0; k < C; ++k) acc[k] += wp * row[u][k];
+            for (int k = 0; k < C; ++k) acc[k] += (p0 + u < P) ? wp * row[u][k] : 0.f;
         }
+    };
+    accumulate(row, 0);                         // unconditional: the loads stay up front
+    for (int p0 = U; p0 < P; p0 += U) {
+        load_rows(row, p0);
+        accumulate(row, p0);
     }
     const float inv = P > 0 ? 1.0f / W : 0.f;
     if (OUT_BF16) {

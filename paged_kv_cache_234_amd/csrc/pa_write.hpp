@@ -1,7 +1,7 @@
 // Writing one new token's K/V row into the pools, shared by pa_kv_append and
 // the decode kernel's fused append.
 //
-// A call moves 8 consecutive head_dim elements (chunk c) of one (token, head):
+// A chunk is 8 consecutive head_dim elements (chunk c) of one (token, head):
 // contiguous stores into the K pool (K[block][head][d / X][offset][d % X],
 // X = 16 bytes of elements) and 8 element stores into the token-minor V tile
 // (V[block][head][d][offset]).  fp8 encoding is an IEEE binary32 divide by
@@ -26,14 +26,37 @@ __device__ __forceinline__ uint32_t encode_e4m3_pair(float x0, float x1, float s
     return pk;
 }
 
-// k_src / v_src: the token's row for this head (D elements of the input type);
-// blk / off: its slot; ksc / vsc: the head's fp8 scales (fp8 caches only)
+// One lane's chunk of a token row as loaded from the input: 8 elements of K
+// and of V (fp32: two 16-byte pieces each).
+template <int CACHE> struct TokenChunk {
+    static constexpr int N = CACHE == kF32 ? 2 : 1;
+    u32x4 k[N], v[N];
+};
+
+// k_src / v_src: the token's row for this head (D elements of the input type)
 template <int CACHE, int D>
-__device__ __forceinline__ void write_token_chunk(const void* k_src, const void* v_src,
-                                                  char* __restrict__ k_cache,
-                                                  char* __restrict__ v_cache, long blk, int off,
-                                                  int h, int num_kv_heads, int c, float ksc,
-                                                  float vsc) {
+__device__ __forceinline__ TokenChunk<CACHE> load_token_chunk(const void* k_src, const void* v_src,
+                                                              int c) {
+    TokenChunk<CACHE> t;
+    if (CACHE == kF32) {
+        const float* ks = static_cast<const float*>(k_src) + 8 * c;
+        const float* vs = static_cast<const float*>(v_src) + 8 * c;
+        t.k[0] = load16_cached(ks);
+        t.k[t.N - 1] = load16_cached(ks + 4);
+        t.v[0] = load16_cached(vs);
+        t.v[t.N - 1] = load16_cached(vs + 4);
+    } else {
+        t.k[0] = load16_cached(static_cast<const uint16_t*>(k_src) + 8 * c);
+        t.v[0] = load16_cached(static_cast<const uint16_t*>(v_src) + 8 * c);
+    }
+    return t;
+}
+
+// blk / off: the token's slot; ksc / vsc: the head's fp8 scales (fp8 caches only)
+template <int CACHE, int D>
+__device__ __forceinline__ void store_token_chunk(const TokenChunk<CACHE>& t, char* k_cache,
+                                                  char* v_cache, long blk, int off, int h,
+                                                  int num_kv_heads, int c, float ksc, float vsc) {
     // element index of K[blk][h][d / X][off][d % X] for d = 8c (X elements per 16 bytes)
     constexpr int X = (CACHE == kF32) ? 4 : (CACHE == kBF16 ? 8 : 16);
     auto kidx = [&](int d) -> long {
@@ -42,32 +65,25 @@ __device__ __forceinline__ void write_token_chunk(const void* k_src, const void*
     const long vdst = ((blk * num_kv_heads + h) * D + 8 * c) * kBlock + off;
 
     if (CACHE == kF32) {
-        const float* ks = static_cast<const float*>(k_src) + 8 * c;
-        const float* vsrc = static_cast<const float*>(v_src) + 8 * c;
-        u32x4 k0 = load16_cached(ks), k1 = load16_cached(ks + 4);
-        u32x4 v0 = load16_cached(vsrc), v1 = load16_cached(vsrc + 4);
         float* kc = reinterpret_cast<float*>(k_cache);
-        *reinterpret_cast<u32x4*>(kc + kidx(8 * c)) = k0;
-        *reinterpret_cast<u32x4*>(kc + kidx(8 * c + 4)) = k1;
+        *reinterpret_cast<u32x4*>(kc + kidx(8 * c)) = t.k[0];
+        *reinterpret_cast<u32x4*>(kc + kidx(8 * c + 4)) = t.k[t.N - 1];
         uint32_t* vd = reinterpret_cast<uint32_t*>(v_cache) + vdst;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vd[e * kBlock] = v0[e];
-            vd[(e + 4) * kBlock] = v1[e];
+            vd[e * kBlock] = t.v[0][e];
+            vd[(e + 4) * kBlock] = t.v[t.N - 1][e];
         }
     } else if (CACHE == kBF16) {
-        u32x4 kv = load16_cached(static_cast<const uint16_t*>(k_src) + 8 * c);
-        u32x4 vv = load16_cached(static_cast<const uint16_t*>(v_src) + 8 * c);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kidx(8 * c)) = kv;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(k_cache) + kidx(8 * c)) = t.k[0];
         uint16_t* vd = reinterpret_cast<uint16_t*>(v_cache) + vdst;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vd[(2 * e) * kBlock] = (uint16_t)(vv[e] & 0xFFFFu);
-            vd[(2 * e + 1) * kBlock] = (uint16_t)(vv[e] >> 16);
+            vd[(2 * e) * kBlock] = (uint16_t)(t.v[0][e] & 0xFFFFu);
+            vd[(2 * e + 1) * kBlock] = (uint16_t)(t.v[0][e] >> 16);
         }
     } else {  // bf16 -> fp8 e4m3
-        u32x4 kv = load16_cached(static_cast<const uint16_t*>(k_src) + 8 * c);
-        u32x4 vv = load16_cached(static_cast<const uint16_t*>(v_src) + 8 * c);
+        const u32x4 kv = t.k[0], vv = t.v[0];
         uint32_t kq[2], vq[2];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -86,6 +102,15 @@ __device__ __forceinline__ void write_token_chunk(const void* k_src, const void*
 #pragma unroll
         for (int e = 0; e < 8; ++e) vd[e * kBlock] = (uint8_t)(vq[e >> 2] >> (8 * (e & 3)));
     }
+}
+
+template <int CACHE, int D>
+__device__ __forceinline__ void write_token_chunk(const void* k_src, const void* v_src,
+                                                  char* k_cache, char* v_cache, long blk, int off,
+                                                  int h, int num_kv_heads, int c, float ksc,
+                                                  float vsc) {
+    store_token_chunk<CACHE, D>(load_token_chunk<CACHE, D>(k_src, v_src, c), k_cache, v_cache,
+                                blk, off, h, num_kv_heads, c, ksc, vsc);
 }
 
 }  // namespace pa

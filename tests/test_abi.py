@@ -130,3 +130,17 @@ def test_multi_query_validation():
     assert call(mq=65) == _lib.PA_ERR_UNSUPPORTED
     assert call(mq=0) == _lib.PA_OK
     assert call(B=0) == _lib.PA_OK
+
+
+def test_decode_append_validation():
+    lib = _lib.load()
+
+    def call(out=FAKE, kn=FAKE, vn=FAKE, sl=FAKE, ps=64, parts=FAKE, B=4):
+        return lib.pa_decode_append(out, FAKE, 1, kn, vn, sl, FAKE, FAKE, 1, None, None, FAKE, 32,
+                                    FAKE, B, 8, 2, 128, 16, 0.1, ps, 4, parts, parts, parts, None)
+
+    assert call(vn=None) == _lib.PA_ERR_ARG                       # append arrays go together
+    assert call(sl=None) == _lib.PA_ERR_ARG
+    assert call(parts=None) == _lib.PA_ERR_ARG
+    assert call(ps=0, out=None) == _lib.PA_ERR_ARG
+    assert call(B=0) == _lib.PA_OK

@@ -12,7 +12,7 @@ from oracle import paged_attention as opa
 from paged_kv_cache_234_amd import (pa_decode, pa_decode_append, pa_decode_splitk_reduce,
                                     pa_kv_append)
 from tests.gpu_helpers import (TOL, as_f64, decode_new_tokens, gpu_pool, host, i32, max_abs_err,
-                               oracle_pool)
+                               oracle_pool, run_decode)
 from workloads import build_workload, make_config
 
 pytestmark = pytest.mark.gpu
@@ -87,3 +87,49 @@ def test_fused_append_skips_tokens_in_shared_blocks():
 @pytest.mark.parametrize("cfg,ps", [(2, 256), (4, 512)])
 def test_fused_append_full_size(cfg, ps):
     _check(make_config(cfg, device="cuda"), ps)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_decode_append_without_append_is_pa_decode(ps):
+    """k_new, v_new and new_slots all None: the launch only decodes, with
+    pa_decode's exact results."""
+    w = build_workload("fn", seed=11 + ps, device="cuda", num_heads=16, num_kv_heads=2,
+                       head_dim=128, decode_lens=LENS)
+    pool = gpu_pool(w)
+    want, parts_w = run_decode(w, pool, ps)
+    q = w.q.contiguous()
+    B, hq, d = q.shape
+    out = torch.empty_like(q)
+    kw = {}
+    if ps:
+        pmax = -(-int(np.max(w.context_lens)) // ps)
+        kw = dict(partition_size=ps, max_partitions=pmax,
+                  part_max=torch.full((B, hq, pmax), float("nan"), device="cuda"),
+                  part_sum=torch.full((B, hq, pmax), float("nan"), device="cuda"),
+                  part_out=torch.full((B, hq, pmax, d), float("nan"), device="cuda"))
+    pa_decode_append(None if ps else out, q, None, None, None, pool.k, pool.v, i32(w.block_tables),
+                     i32(w.context_lens), w.scale, **kw)
+    if ps:
+        pa_decode_splitk_reduce(out, kw["part_max"], kw["part_sum"], kw["part_out"],
+                                i32(w.context_lens), ps)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+
+
+def test_fused_append_ignores_a_slot_off_the_table():
+    """A new_slots entry that is not the table's slot of position L - 1
+    writes nothing."""
+    w = build_workload("fo", seed=12, device="cuda", num_heads=8, num_kv_heads=2, head_dim=128,
+                       decode_lens=[40, 70, 5])
+    pool = gpu_pool(w, without_new=True)
+    before_k, before_v = pool.k.clone(), pool.v.clone()
+    k_new, v_new, slots = decode_new_tokens(w)
+    bad = slots.clone()
+    bad[:] = torch.where(bad >= 0, bad + 1, bad)       # the next slot: off the table's position
+    q = w.q.contiguous()
+    out = torch.empty_like(q)
+    pa_decode_append(out, q, k_new, v_new, bad, pool.k, pool.v, i32(w.block_tables),
+                     i32(w.context_lens), w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k.view(torch.uint8), before_k.view(torch.uint8))
+    assert torch.equal(pool.v.view(torch.uint8), before_v.view(torch.uint8))
