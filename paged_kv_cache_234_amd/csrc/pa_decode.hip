@@ -21,9 +21,11 @@
 //
 // Work decomposition.  A work item is (row, virtual head, partition).  Tiles
 // of TT positions are numbered row-major, then virtual head, then position;
-// each workgroup builds the prefix of per-row tile counts in LDS.  Workgroup k
-// takes the whole items whose first tile lies in [T k / NWG, T (k+1) / NWG);
-// its NW wavefronts split that run into NW equal runs of tiles.  A wavefront
+// each workgroup builds the prefix of per-row tile counts in LDS.  With s(g)
+// the item start nearest to tile g, workgroup k takes the whole items whose
+// first tile lies in [s(T k / NWG), s(T (k+1) / NWG)), which is within half
+// an item of an equal share; its NW wavefronts split that run into NW equal
+// runs of tiles.  A wavefront
 // streams its tiles back to back: the next tile's K/V loads -- across item
 // boundaries too -- are in flight while the current tile is multiplied, a
 // finished item writes its partial (or output) straight from registers, and
@@ -185,19 +187,25 @@ void decode_kernel(DecodeArgs a) {
         return max(0, n - row_skip(r));
     };
     // tiles of one (virtual) head of row r
-    auto row_head_tiles = [&](int r) {
+    auto head_tiles_of = [&](int r) {
         const int n = row_items(r);
         if (n == 0) return 0;
         const int last = row_skip(r) + n - 1;
         return (n - 1) * tpi + (s_len[r] - last * PS + TT - 1) / TT;
     };
+    // plain decode keeps it in s_aux (otherwise unused) once the prefix is built
+    auto row_head_tiles = [&](int r) { return PLAIN ? s_aux[r] : head_tiles_of(r); };
 
     // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
     const int per = (R + NT - 1) / NT;
     const int r0 = tid * per;
     int local = 0;
     for (int k = 0; k < per; ++k)
-        if (r0 + k < R) local += row_heads(r0 + k) * row_head_tiles(r0 + k);
+        if (r0 + k < R) {
+            const int th = head_tiles_of(r0 + k);
+            if (PLAIN) s_aux[r0 + k] = th;
+            local += row_heads(r0 + k) * th;
+        }
     int incl = local;                                     // inclusive scan within the wave
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -217,7 +225,7 @@ void decode_kernel(DecodeArgs a) {
         for (int k = 0; k < per; ++k)
             if (r0 + k < R) {
                 s_tpre[r0 + k] = run;
-                run += row_heads(r0 + k) * row_head_tiles(r0 + k);
+                run += row_heads(r0 + k) * (PLAIN ? s_aux[r0 + k] : head_tiles_of(r0 + k));
             }
         if (tid == 0) s_tpre[R] = total_tiles;
     }
@@ -234,43 +242,66 @@ void decode_kernel(DecodeArgs a) {
     __syncthreads();
 
     // ---- tile ranges ----------------------------------------------------------
-    const long T = total_tiles;
+    // Tile numbers fit in 32 bits (the prefix lives in an int table); the
+    // range arithmetic stays in 32-bit integers, off the 64-bit divide path.
+    const int T = total_tiles;
 
-    // row r with tpre[r] <= g < tpre[r+1] (g < T): the largest such r,
-    // searched 64 candidates at a time (two LDS round trips for 4096 rows).
-    // tpre is nondecreasing, so the lanes whose candidate qualifies form a
-    // prefix of the wave.
-    auto row_of = [&](long g) {
-        int lo = 0, span = R;
-        while (span > 1) {
-            const int stride = (span + kWave - 1) / kWave;
-            const int idx = lo + lane * stride;
-            const bool ok = idx < lo + span && s_tpre[idx] <= g;
-            const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok));
-            const int end = lo + span;
-            lo += (cnt - 1) * stride;
-            span = min(stride, end - lo);
+    // For two tiles ga, gb < T at once (their LDS reads overlap): the row r
+    // with tpre[r] <= g < tpre[r+1], i.e. the largest such r, searched 64
+    // candidates at a time (two LDS round trips for 4096 rows).  tpre is
+    // nondecreasing, so the lanes whose candidate qualifies form a prefix of
+    // the wave.
+    auto row_of2 = [&](int ga, int gb, int& ra, int& rb) {
+        int loa = 0, spa = R, lob = 0, spb = R;
+        while (spa > 1 || spb > 1) {
+            const int sta = (spa + kWave - 1) / kWave, stb = (spb + kWave - 1) / kWave;
+            const int ia = loa + lane * sta, ib = lob + lane * stb;
+            const bool oka = spa > 1 && ia < loa + spa && s_tpre[ia] <= ga;
+            const bool okb = spb > 1 && ib < lob + spb && s_tpre[ib] <= gb;
+            const int ca = __builtin_popcountll(__builtin_amdgcn_ballot_w64(oka));
+            const int cb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(okb));
+            if (spa > 1) {
+                const int end = loa + spa;
+                loa += (ca - 1) * sta;
+                spa = min(sta, end - loa);
+            }
+            if (spb > 1) {
+                const int end = lob + spb;
+                lob += (cb - 1) * stb;
+                spb = min(stb, end - lob);
+            }
         }
-        return lo;
+        ra = loa;
+        rb = lob;
     };
-    // first tile of the first item starting at or after tile g
-    auto item_start_at_or_after = [&](long g) -> long {
-        if (g >= T) return T;
-        const int r = row_of(g);
+    // the item start nearest to tile g < T in row r (the earlier one on a tie)
+    auto nearest_item_start = [&](int g, int r) -> int {
         const int th = row_head_tiles(r);
-        const long base = s_tpre[r];
-        const int vh = (int)((g - base) / th);
-        const int j = (int)(g - base - (long)vh * th);
-        const int p = (j + tpi - 1) / tpi;
-        if (p < row_items(r)) return base + (long)vh * th + (long)p * tpi;
-        return base + (long)(vh + 1) * th;
+        const int base = s_tpre[r];
+        const int vh = (g - base) / th;
+        const int head0 = base + vh * th;
+        const int p = (g - head0) / tpi;
+        const int before = head0 + p * tpi;                        // item holding g
+        const int after = p + 1 < row_items(r) ? before + tpi : head0 + th;
+        return (g - before <= after - g) ? before : after;
     };
-    const long nwg = gridDim.x;
-    const long wg_a = item_start_at_or_after(T * (long)blockIdx.x / nwg);
-    const long wg_e = item_start_at_or_after(T * ((long)blockIdx.x + 1) / nwg);
+    // T k / NWG, exact: the double product is below 2^53 and a non-integral
+    // quotient stays at least 1 / (T k) away from the next integer
+    auto share = [&](int k) { return (int)((double)T * k / (double)gridDim.x); };
+    const int sa = share(blockIdx.x), se = share(blockIdx.x + 1);
+    int wg_a = 0, wg_e = 0;
+    if (T > 0) {
+        int rsa, rse;
+        row_of2(min(sa, T - 1), min(se, T - 1), rsa, rse);
+        wg_a = sa >= T ? T : nearest_item_start(sa, rsa);
+        wg_e = se >= T ? T : nearest_item_start(se, rse);
+    }
     auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
-    const long g0 = wave_start(wave), g1 = wave_start(wave + 1);
-    const int ntiles = (int)(g1 - g0);
+    const int g0 = wave_start(wave), g1 = wave_start(wave + 1);
+    const int ntiles = g1 - g0;
+    // rows of this wavefront's first and last tiles
+    int rg0 = 0, rg1 = 0;
+    if (ntiles > 0) row_of2(g0, g1 - 1, rg0, rg1);
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
     // only one that reads the block of position L_b - 1 for head h -- writes
@@ -279,15 +310,14 @@ void decode_kernel(DecodeArgs a) {
     // later K/V loads of that block return the new token without a wait.
     if (PLAIN && a.new_slots != nullptr && ntiles > 0) {
         constexpr int IB = KIND == kF32 ? 4 : 2;          // input element bytes
-        const int r_first = row_of(g0), r_last = row_of(g1 - 1);
-        for (int r = r_first; r <= r_last; ++r) {
+        for (int r = rg0; r <= rg1; ++r) {
             const int th = row_head_tiles(r);
             if (th == 0) continue;
-            const long base = s_tpre[r];
+            const int base = s_tpre[r];
             // first head whose last tile, base + (h + 1) * th - 1, is at or after g0
-            const long x = g0 - base + 1;
-            const int h0 = x <= 0 ? 0 : (int)std::min<long>(Hkv, (x + th - 1) / th - 1);
-            if (h0 >= Hkv || base + (long)(h0 + 1) * th - 1 >= g1) continue;
+            const int x = g0 - base + 1;
+            const int h0 = x <= 0 ? 0 : min(Hkv, (x + th - 1) / th - 1);
+            if (h0 >= Hkv || base + (h0 + 1) * th - 1 >= g1) continue;
             // only the slot the table gives position L - 1 (the block read below)
             const int lp = max(s_len[r] - 1, 0);
             const int slot = load_invariant(a.new_slots + r);
@@ -295,7 +325,7 @@ void decode_kernel(DecodeArgs a) {
                                             lp / kBlock) * kBlock + lp % kBlock;
             if (slot < 0 || slot != want) continue;
             for (int h = h0; h < Hkv; ++h) {
-                if (base + (long)(h + 1) * th - 1 >= g1) break;
+                if (base + (h + 1) * th - 1 >= g1) break;
                 const long row = ((long)r * Hkv + h) * D * IB;
                 const float ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
                 const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
@@ -364,13 +394,13 @@ void decode_kernel(DecodeArgs a) {
 
     Cursor cc;          // tile being computed
     if (ntiles > 0) {
-        const int r = row_of(g0);
+        const int r = rg0;
         const int th = row_head_tiles(r);
-        const long base = s_tpre[r];
-        const int vh = (int)((g0 - base) / th);
-        const int j = (int)(g0 - base - (long)vh * th);
+        const int base = s_tpre[r];
+        const int vh = (g0 - base) / th;
+        const int j = g0 - base - vh * th;
         const int p = j / tpi;
-        set_item(cc, r, vh, p, base + (long)vh * th + (long)p * tpi);
+        set_item(cc, r, vh, p, base + vh * th + p * tpi);
         cc.jj = j - p * tpi;
     }
     bool tail_open = false;       // this wave's last piece ends inside its item
@@ -653,6 +683,8 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     hipError_t e = hipSuccess;
     const int kind = cache_kind(cache_dtype);
     auto tiles = [&](int tt) { return items_bound * ((a.partition_size + tt - 1) / tt); };
+    // tile numbers are 32-bit in the kernel
+    if (tiles(16) > 0x7fffffffL) return PA_ERR_UNSUPPORTED;
 #define PA_LAUNCH(K, DD, TT)                                                          \
     (wide ? launch_decode<K, DD, 2, false>(a, tiles(TT), stream)                      \
           : launch_decode<K, DD, 1, true>(a, tiles(TT), stream))
