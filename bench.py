@@ -284,6 +284,8 @@ def main():
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    result_entry = ("pa_decode_append" if fused else "pa_decode_multi" if spec else
+                    "pa_decode_cascade" if cascade else "pa_decode")
     result = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -305,8 +307,7 @@ def main():
             "new_tokens": int(len(w.new_slots)),
             "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
             "pool_blocks": w.num_blocks, "layer_copies": R,
-            "decode_entry": ("pa_decode_append" if fused else "pa_decode_multi" if spec else
-                             "pa_decode_cascade" if cascade else "pa_decode"),
+            "decode_entry": result_entry,
             "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (
@@ -325,14 +326,13 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode_append" if fused else "pa_decode_multi" if spec else
-                       "pa_decode_cascade" if cascade else "pa_decode"),
+            "kernel": result_entry,
             "duration_us": round(decode_ms * 1e3, 3),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w.name, ps),
+            "traffic": measured_traffic(w.name, ps, result_entry),
         },
     }
     if has_prefill:
@@ -351,19 +351,21 @@ def decode_source_hash():
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_234_amd", "csrc")
-    for f in ("pa_decode.hip", "pa_tiles.hpp", "pa_device.hpp", "pa_internal.hpp"):
+    for f in ("pa_decode.hip", "pa_tiles.hpp", "pa_device.hpp", "pa_internal.hpp", "pa_write.hpp"):
         with open(os.path.join(csrc, f)) as fh:
             lines = [re.sub(r"//.*", "", ln).rstrip() for ln in fh.read().splitlines()]
         h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()
 
 
-def measured_traffic(workload, ps):
+def measured_traffic(workload, ps, entry):
     """HBM bytes per decode launch from the FETCH_SIZE / WRITE_SIZE counter
     runs summarised under profiles/ (copy-calibrated), or None when no
-    summary matches this workload, partition size and decode source."""
+    summary matches this workload, partition size, entry point and decode
+    source."""
     import glob
-    want = {"workload": workload, "partition_size": str(ps), "decode_source_sha256": decode_source_hash()}
+    want = {"workload": workload, "partition_size": str(ps), "decode_entry": entry,
+            "decode_source_sha256": decode_source_hash()}
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.md"))):
         kv = {}
         with open(path) as fh:
