@@ -30,6 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-decode KV GB/s (% of HBM peak) + µs per layer-step, 1×MI355X"
 HBM_PEAK_GBPS = 8000.0
+# Plain decode steps read their launch prologue from a plan made once per
+# model step for all its layers: one pa_decode_plan per PLAN_LAYERS
+# layer-steps (32 is Llama-3-8B's layer count; Qwen2.5-3B has 36).
+PLAN_LAYERS = 32
 DEFAULT_PS = {1: 64, 2: 256, 3: 256, 4: 512, 5: 256}
 
 
@@ -47,6 +51,9 @@ def parse():
     ap.add_argument("--no-fuse-append", action="store_true",
                     help="append the decode tokens with pa_kv_append before pa_decode instead of "
                          "pa_decode_append's single launch")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="plain decode launches compute their prologue instead of reading a "
+                         "per-step plan")
     ap.add_argument("--no-cascade", action="store_true",
                     help="decode prefix-sharing batches with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--eager", action="store_true",
@@ -67,7 +74,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_cache_234_amd import (KVPool, pa_decode, pa_decode_append, pa_decode_cascade,
+    from paged_kv_cache_234_amd import (KVPool, decode_plan_buffer, pa_decode, pa_decode_append,
+                                        pa_decode_plan, pa_decode_cascade,
                                         pa_decode_multi, pa_decode_splitk_reduce, pa_prefill_chunk,
                                         pa_selftest)
     from workloads import make_config, make_spec_verify
@@ -143,6 +151,12 @@ def main():
                 j += 1
         ridx = torch.as_tensor(rows, device=dev)
         fk, fv, fslots = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous(), i32(fslots)
+    planned = fused and not args.no_plan
+    plan = decode_plan_buffer(B, pools[0].k, d) if planned else None
+
+    def make_plan():
+        pa_decode_plan(plan, bt, lens, w.num_heads, pools[0].k, pools[0].v, partition_size=ps,
+                       max_partitions=pmax)
     if has_prefill:
         qp = w.q_prefill.contiguous()
         outp = torch.empty_like(qp)
@@ -157,6 +171,8 @@ def main():
         pool = pools[layer % R]
         if ev is not None:
             ev[0].record(stream)
+        if planned and layer % PLAN_LAYERS == 0:
+            make_plan()
         if not fused:
             pool.append(new_k, new_v, new_slots)
         if ev is not None:
@@ -182,7 +198,7 @@ def main():
             pa_decode_append(out if ps == 0 else None, q, fk, fv, fslots, pool.k, pool.v, bt, lens,
                              w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
                              max_partitions=pmax, part_max=part_max, part_sum=part_sum,
-                             part_out=part_out)
+                             part_out=part_out, plan=plan)
         elif spec:
             pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
                             part_sum, part_out, pool.k_scale, pool.v_scale)
@@ -196,6 +212,8 @@ def main():
         else:
             pa_decode(out, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale)
 
+    if planned:
+        make_plan()
     for i in range(max(args.warmup, 1)):
         step(i)
         decode_only(i)
@@ -257,7 +275,8 @@ def main():
     for i in range(args.steps):
         step(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
-    names = (["(append fused)", "decode_append"] if fused else ["kv_append", "decode"]) + \
+    names = (["(append fused)" + (", plan / %d layers" % PLAN_LAYERS if planned else ""),
+              "decode_append"] if fused else ["kv_append", "decode"]) + \
         ["splitk_reduce", "prefill_chunk"]
     names = names[:nev - 1]
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
@@ -308,6 +327,7 @@ def main():
             "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
             "pool_blocks": w.num_blocks, "layer_copies": R,
             "decode_entry": result_entry,
+            "plan": ("pa_decode_plan once per %d layer-steps" % PLAN_LAYERS) if planned else None,
             "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (

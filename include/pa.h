@@ -154,6 +154,14 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
  *                  in the pool (e.g. a token inside a prefix-shared block).
  *                  Any other value writes nothing.
  *                  k_new, v_new and new_slots all NULL: no append.
+ *   plan           NULL, or a launch plan pa_decode_plan made for the same
+ *                  block_tables, context_lens, batch, heads, head_dim,
+ *                  cache dtype, partition_size and max_partitions on this
+ *                  device: the launch then skips its prologue (see
+ *                  pa_decode_plan).  A plan whose header does not match
+ *                  these arguments makes the launch do nothing.
+ *   plan_bytes     the plan buffer's size; less than pa_decode_plan_bytes
+ *                  for this batch returns PA_ERR_ARG
  * Other arguments, outputs, layouts and errors as pa_decode; the pools are
  * written (fp8 caches encode as pa_kv_append does).
  */
@@ -167,7 +175,34 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
                              int32_t block_size, float scale,
                              int32_t partition_size, int32_t max_partitions,
                              float* part_max, float* part_sum, float* part_out,
-                             hipStream_t stream);
+                             const int32_t* plan, size_t plan_bytes, hipStream_t stream);
+
+/*
+ * Launch plan for pa_decode_append.  Every layer of a decode step runs the
+ * same batch: the same context lengths and block tables.  The decode
+ * prologue depends only on those and the launch shape: the row table in LDS,
+ * the prefix of tiles, each workgroup's and wavefront's tile range, and the
+ * block ids of each wavefront's first tile.  pa_decode_plan computes it once
+ * with the decode kernel's own prologue and writes it to `plan`.
+ * pa_decode_append(..., plan) then reads it instead, which saves the
+ * per-launch prologue and its block-id round trip for every layer.  This is
+ * the plan-once, run-per-layer split that the engines the pages build on use
+ * (llm-infer, "What It Does": the decode step replayed for every layer).
+ *   plan        int32 device buffer of at least pa_decode_plan_bytes(batch,
+ *               cache_dtype, head_dim) bytes (the workgroup count depends on
+ *               the device's compute units)
+ *   other arguments as pa_decode_append (Q, K/V and scales are not read)
+ * The plan stays valid while context_lens and the first ceil(L_b / 16)
+ * block-table entries of every row are unchanged.  It follows the stream:
+ * the plan launch must precede its users on that stream, or be otherwise
+ * ordered before them.
+ */
+size_t pa_decode_plan_bytes(int32_t batch, pa_dtype_t cache_dtype, int32_t head_dim);
+pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, pa_dtype_t cache_dtype, int32_t partition_size,
+                           int32_t max_partitions, hipStream_t stream);
 
 /*
  * Shared-prefix ("cascade") split-K decode: the same partials as pa_decode

@@ -21,7 +21,7 @@ BLOCK_SIZE = 16
 
 EXPORTED = (
     "pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade", "pa_decode_multi",
-    "pa_decode_splitk_reduce", "pa_prefill_chunk",
+    "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_decode_plan", "pa_decode_plan_bytes",
     "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest",
 )
 
@@ -48,7 +48,12 @@ def load(path=LIB_PATH):
     lib.pa_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                               f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_append.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
-                                     i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
+                                     i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
+                                     ctypes.c_size_t, st]
+    lib.pa_decode_plan.argtypes = [vp, ctypes.c_size_t, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, st]
+    lib.pa_decode_plan_bytes.argtypes = [i32, i32, i32]
+    lib.pa_decode_plan_bytes.restype = ctypes.c_size_t
     lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
     lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
@@ -62,7 +67,8 @@ def load(path=LIB_PATH):
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_selftest.argtypes = []
     for fn in ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade",
-               "pa_decode_multi", "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_selftest"):
+               "pa_decode_multi", "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_decode_plan",
+               "pa_selftest"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -130,6 +136,41 @@ def pa_decode_workspace_bytes(batch, num_heads, head_dim, max_partitions):
     return int(load().pa_decode_workspace_bytes(batch, num_heads, head_dim, max_partitions))
 
 
+def pa_decode_plan_bytes(batch, k_cache, head_dim):
+    """Bytes of a launch plan for a batch over pools of k_cache's dtype."""
+    return int(load().pa_decode_plan_bytes(int(batch), _dt(k_cache), int(head_dim)))
+
+
+def decode_plan_buffer(batch, k_cache, head_dim, device="cuda"):
+    """An int32 device buffer large enough for pa_decode_plan."""
+    n = -(-pa_decode_plan_bytes(batch, k_cache, head_dim) // 4)
+    return torch.empty(max(n, 1), dtype=torch.int32, device=device)
+
+
+def _plan_ptr(plan):
+    if plan is None:
+        return None
+    if plan.dtype != torch.int32:
+        raise TypeError("plan must be int32")
+    return _ptr(plan)
+
+
+def pa_decode_plan(plan, block_tables, context_lens, num_heads, k_cache, v_cache, partition_size=0,
+                   max_partitions=1, stream=None):
+    """Fill `plan` (from decode_plan_buffer) with the decode prologue of this
+    batch, for pa_decode_append(..., plan=plan) launches with the same
+    arguments."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    B = context_lens.numel()
+    if block_tables.shape[0] != B:
+        raise ValueError("inconsistent decode shapes")
+    st = load().pa_decode_plan(_plan_ptr(plan), plan.numel() * 4, _i32(block_tables, "block_tables"),
+                               block_tables.shape[1], _i32(context_lens, "context_lens"), B,
+                               int(num_heads), hkv, d, _dt(k_cache), int(partition_size),
+                               int(max_partitions), _stream(stream))
+    _check("pa_decode_plan", st)
+
+
 def pa_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=None,
                  stream=None):
     """k_new, v_new [T, Hkv, D]; pools as in include/pa.h; slot_mapping int32 [T]."""
@@ -174,10 +215,12 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_sca
 
 def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_tables,
                      context_lens, scale, k_scale=None, v_scale=None, partition_size=0,
-                     max_partitions=1, part_max=None, part_sum=None, part_out=None, stream=None):
+                     max_partitions=1, part_max=None, part_sum=None, part_out=None, plan=None,
+                     stream=None):
     """pa_kv_append of each sequence's newest token (k_new, v_new [B, Hkv, D],
     new_slots int32 [B], -1 to skip; all three None: no append) and
-    pa_decode, in one launch."""
+    pa_decode, in one launch.  plan: a buffer pa_decode_plan filled for the
+    same batch and arguments (skips the launch's prologue)."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     B, hq = q.shape[0], q.shape[1]
     if q.shape[2] != d or block_tables.shape[0] != B or context_lens.numel() != B:
@@ -206,7 +249,8 @@ def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_ta
                                  block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,
                                  hkv, d, bs, float(scale), int(partition_size),
                                  int(max_partitions), _ptr(part_max), _ptr(part_sum),
-                                 _ptr(part_out), _stream(stream))
+                                 _ptr(part_out), _plan_ptr(plan),
+                                 0 if plan is None else plan.numel() * 4, _stream(stream))
     _check("pa_decode_append", st)
 
 

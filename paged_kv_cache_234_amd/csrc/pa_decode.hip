@@ -32,6 +32,7 @@
 // an item cut between wavefronts is merged through LDS by the wavefront that
 // holds its first tile.
 #include <algorithm>
+#include <type_traits>
 
 #include "pa_internal.hpp"
 #include "pa_tiles.hpp"
@@ -41,6 +42,28 @@ namespace pa {
 
 constexpr int kMaxDecodeRows = 4096;
 constexpr int kMaxMultiQuery = 64;     // query tokens per sequence in pa_decode_multi
+
+// Launch plan.  The decode prologue (row table, tile prefix, workgroup and
+// wavefront ranges, the first tile's block ids) depends only on the context
+// lengths, the block tables and the launch shape, which every layer of a
+// decode step shares.  A plan holds it as int32 words:
+//   [0, 16)             header (kPlan* fields below)
+//   [16, 16 + B)        context length per row (cut as the prologue cuts it)
+//   [16 + B, 16 + 2B)   tiles per KV head per row
+//   [16 + 2B, 17 + 3B)  exclusive prefix of tiles (B + 1 entries)
+//   then, 16-aligned, 16 words per wavefront (grid x 4): first and end tile,
+//   its workgroup's first and end tile, the rows of its first and last tile,
+//   the block ids of its first tile (4 words) and of its second (4 words).
+enum { kRun = 0, kMakePlan = 1, kUsePlan = 2 };
+constexpr int kPlanMagic = 0x50414450;
+enum {
+    kPlanMagicW, kPlanBatch, kPlanKvHeads, kPlanPS, kPlanMaxPart, kPlanTT, kPlanGrid, kPlanNW,
+    kPlanMaxBlocks, kPlanSplit, kPlanTiles, kPlanHeadDim, kPlanHeader = 16
+};
+constexpr int kPlanWave = 16;
+__host__ __device__ constexpr long plan_waves_offset(int batch) {
+    return ((long)kPlanHeader + 3L * batch + 1 + 15) / 16 * 16;
+}
 
 struct DecodeArgs {
     void* out;
@@ -72,6 +95,10 @@ struct DecodeArgs {
     const int32_t* new_slots;
     char* k_cache_w;
     char* v_cache_w;
+    // launch plan (plain decode): written by pa_decode_plan's launch, read
+    // in place of the prologue by later launches over the same batch
+    const int32_t* plan;
+    int32_t* plan_out;
     int max_blocks_per_seq;
     int batch;
     int num_heads;
@@ -99,9 +126,10 @@ template <int NVT, int NC> struct SegSlot {
 // NC * 16 / G members or query positions.
 // PLAIN: sequence rows only (pa_decode); the group and multi-query row code
 // is compiled out.
-template <int KIND, int D, int NW, int NC, bool PLAIN>
+template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
+    static_assert(PLAIN || MODE == kRun, "plans cover plain decode only");
     using Ops = TileOps<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int TT = Ops::TT, TB = Ops::TB, NVT = Ops::NVT, ELEM = Ops::ELEM;
@@ -128,6 +156,47 @@ void decode_kernel(DecodeArgs a) {
     const int mpv = mpc * NC;                            // ... per virtual head
     const bool multi = !PLAIN && a.query_start_loc != nullptr;
 
+    // what the prologue settles: total tiles, this workgroup's and this
+    // wavefront's tile ranges, the rows of the wavefront's first and last tile
+    int T = 0, wg_a = 0, wg_e = 0, g0 = 0, g1 = 0, rg0 = 0, rg1 = 0;
+    int plan_ids[2][Ops::TB];                    // block ids of the first two tiles (from a plan)
+    bool plan_ok = true;
+    if constexpr (MODE == kUsePlan) {
+        // header and this wavefront's words: scalar loads; the row table
+        // goes to LDS.  A plan made for other arguments leaves no work.
+        const int32_t* pl = a.plan;
+        const int eff_ps = PS, eff_mp = a.max_partitions;
+        plan_ok = load_invariant(pl + kPlanMagicW) == kPlanMagic &&
+                  load_invariant(pl + kPlanBatch) == B && load_invariant(pl + kPlanKvHeads) == Hkv &&
+                  load_invariant(pl + kPlanPS) == eff_ps &&
+                  load_invariant(pl + kPlanMaxPart) == eff_mp &&
+                  load_invariant(pl + kPlanTT) == TT &&
+                  load_invariant(pl + kPlanGrid) == (int)gridDim.x &&
+                  load_invariant(pl + kPlanNW) == NW &&
+                  load_invariant(pl + kPlanMaxBlocks) == a.max_blocks_per_seq &&
+                  load_invariant(pl + kPlanSplit) == a.split &&
+                  load_invariant(pl + kPlanHeadDim) == D;
+        const int32_t* wv = pl + plan_waves_offset(B) + ((long)blockIdx.x * NW + wave) * kPlanWave;
+        T = load_invariant(pl + kPlanTiles);
+        g0 = load_invariant(wv + 0);
+        g1 = load_invariant(wv + 1);
+        wg_a = load_invariant(wv + 2);
+        wg_e = load_invariant(wv + 3);
+        rg0 = load_invariant(wv + 4);
+        rg1 = load_invariant(wv + 5);
+#pragma unroll
+        for (int j = 0; j < Ops::TB; ++j) {
+            plan_ids[0][j] = load_invariant(wv + 6 + j);
+            plan_ids[1][j] = load_invariant(wv + 10 + j);
+        }
+        for (int r = tid; r < B; r += NT) {
+            s_len[r] = pl[kPlanHeader + r];
+            s_aux[r] = pl[kPlanHeader + B + r];
+            s_tpre[r] = pl[kPlanHeader + 2 * B + r];
+        }
+        if (tid == 0) s_tpre[B] = pl[kPlanHeader + 3 * B];
+        if (!plan_ok) g0 = g1 = wg_a = wg_e = 0;
+    } else {
     // ---- row table in LDS -------------------------------------------------------
     // Group descriptors are read together with the context lengths, and a
     // group's member list in batches of 8 independent loads, so the prologue
@@ -172,6 +241,7 @@ void decode_kernel(DecodeArgs a) {
             }
         }
     }
+    }
     __syncthreads();
 
     auto row_skip = [&](int r) { return (!PLAIN && r < B && !multi) ? s_aux[r] : 0; };
@@ -196,6 +266,20 @@ void decode_kernel(DecodeArgs a) {
     // plain decode keeps it in s_aux (otherwise unused) once the prefix is built
     auto row_head_tiles = [&](int r) { return PLAIN ? s_aux[r] : head_tiles_of(r); };
 
+    // single pass: sequences with L = 0 have no tile; their rows are zeros
+    auto zero_empty_rows = [&]() {
+        if (a.split) return;
+        const long rows = (long)B * a.num_heads * D;
+        for (long r = (long)blockIdx.x * NT + tid; r < rows; r += (long)gridDim.x * NT) {
+            if (a.context_lens[r / ((long)a.num_heads * D)] <= 0) {
+                if (KIND == kF32) reinterpret_cast<float*>(a.out)[r] = 0.f;
+                else reinterpret_cast<uint16_t*>(a.out)[r] = 0;
+            }
+        }
+    };
+    if constexpr (MODE == kUsePlan) {
+        zero_empty_rows();
+    } else {
     // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
     const int per = (R + NT - 1) / NT;
     const int r0 = tid * per;
@@ -229,22 +313,13 @@ void decode_kernel(DecodeArgs a) {
             }
         if (tid == 0) s_tpre[R] = total_tiles;
     }
-    // single pass: sequences with L = 0 have no tile; their rows are zeros
-    if (!a.split) {
-        const long rows = (long)B * a.num_heads * D;
-        for (long r = (long)blockIdx.x * NT + tid; r < rows; r += (long)gridDim.x * NT) {
-            if (a.context_lens[r / ((long)a.num_heads * D)] <= 0) {
-                if (KIND == kF32) reinterpret_cast<float*>(a.out)[r] = 0.f;
-                else reinterpret_cast<uint16_t*>(a.out)[r] = 0;
-            }
-        }
-    }
+    if constexpr (MODE == kRun) zero_empty_rows();
     __syncthreads();
 
     // ---- tile ranges ----------------------------------------------------------
     // Tile numbers fit in 32 bits (the prefix lives in an int table); the
     // range arithmetic stays in 32-bit integers, off the 64-bit divide path.
-    const int T = total_tiles;
+    T = total_tiles;
 
     // For two tiles ga, gb < T at once (their LDS reads overlap): the row r
     // with tpre[r] <= g < tpre[r+1], i.e. the largest such r, searched 64
@@ -289,26 +364,26 @@ void decode_kernel(DecodeArgs a) {
     // quotient stays at least 1 / (T k) away from the next integer
     auto share = [&](int k) { return (int)((double)T * k / (double)gridDim.x); };
     const int sa = share(blockIdx.x), se = share(blockIdx.x + 1);
-    int wg_a = 0, wg_e = 0;
     if (T > 0) {
         int rsa, rse;
         row_of2(min(sa, T - 1), min(se, T - 1), rsa, rse);
         wg_a = sa >= T ? T : nearest_item_start(sa, rsa);
         wg_e = se >= T ? T : nearest_item_start(se, rse);
     }
-    auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
-    const int g0 = wave_start(wave), g1 = wave_start(wave + 1);
-    const int ntiles = g1 - g0;
+    g0 = wg_a + (wg_e - wg_a) * wave / NW;
+    g1 = wg_a + (wg_e - wg_a) * (wave + 1) / NW;
     // rows of this wavefront's first and last tiles
-    int rg0 = 0, rg1 = 0;
-    if (ntiles > 0) row_of2(g0, g1 - 1, rg0, rg1);
+    if (g1 > g0) row_of2(g0, g1 - 1, rg0, rg1);
+    }
+    auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
+    const int ntiles = g1 - g0;
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
     // only one that reads the block of position L_b - 1 for head h -- writes
     // b's new token for head h there before loading anything.  A wavefront's
     // vector memory accesses to one address are performed in order, so its
     // later K/V loads of that block return the new token without a wait.
-    if (PLAIN && a.new_slots != nullptr && ntiles > 0) {
+    if (PLAIN && MODE != kMakePlan && a.new_slots != nullptr && ntiles > 0) {
         constexpr int IB = KIND == kF32 ? 4 : 2;          // input element bytes
         for (int r = rg0; r <= rg1; ++r) {
             const int th = row_head_tiles(r);
@@ -402,6 +477,49 @@ void decode_kernel(DecodeArgs a) {
         const int p = j / tpi;
         set_item(cc, r, vh, p, base + vh * th + p * tpi);
         cc.jj = j - p * tpi;
+    }
+
+    // ---- plan launch: record what this prologue found, then stop ----------
+    if constexpr (MODE == kMakePlan) {
+        int32_t* pl = a.plan_out;
+        int32_t* wv = pl + plan_waves_offset(B) + ((long)blockIdx.x * NW + wave) * kPlanWave;
+        int w = 0;
+        // block ids of the first two tiles, as the load cursor would fetch them
+        auto tile_ids = [&](const Cursor& c, int at) {
+            const int32_t* btr = a.block_tables + (long)c.r * a.max_blocks_per_seq;
+            const int lb = (c.tb + c.jj * TT) / kBlock, last = (c.te - 1) / kBlock;
+            if (lane >= at && lane < at + TB) w = btr[min(lb + lane - at, last)];
+        };
+        if (ntiles > 0) tile_ids(cc, 6);
+        if (ntiles > 1) {
+            Cursor c1 = cc;
+            advance(c1);
+            tile_ids(c1, 10);
+        }
+        const int vals[6] = {g0, g1, wg_a, wg_e, rg0, rg1};
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (lane == k) w = vals[k];
+        if (lane < kPlanWave) wv[lane] = w;
+        if (blockIdx.x == 0) {
+            for (int r = tid; r < B; r += NT) {
+                pl[kPlanHeader + r] = s_len[r];
+                pl[kPlanHeader + B + r] = s_aux[r];
+                pl[kPlanHeader + 2 * B + r] = s_tpre[r];
+            }
+            if (tid < kPlanHeader) {
+                const int hdr[kPlanHeader] = {kPlanMagic, B, Hkv, PS, a.max_partitions, TT,
+                                              (int)gridDim.x, NW, a.max_blocks_per_seq, a.split,
+                                              T, D, 0, 0, 0, 0};
+                int v = 0;
+#pragma unroll
+                for (int k = 0; k < kPlanHeader; ++k)
+                    if (tid == k) v = hdr[k];
+                pl[tid] = v;
+            }
+            if (tid == 0) pl[kPlanHeader + 3 * B] = T;
+        }
+        return;
     }
     bool tail_open = false;       // this wave's last piece ends inside its item
     Cursor tail_item;
@@ -544,7 +662,8 @@ void decode_kernel(DecodeArgs a) {
         };
         // load the tile under the load cursor and move the cursor on; the
         // next tile's block ids and (entering an item) Q go out first
-        auto issue = [&](typename Ops::Regs& r) {
+        // FIRST: the launch's first load, whose successor's block ids a plan holds
+        auto issue = [&](typename Ops::Regs& r, auto first) {
             const long hoff = (long)lc.h * head_stride;
             int ph[TB];
 #pragma unroll
@@ -554,7 +673,12 @@ void decode_kernel(DecodeArgs a) {
                 advance(lc);
                 if (lc.r != orow)
                     bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
-                fetch_ids();
+                if constexpr (MODE == kUsePlan && decltype(first)::value) {
+#pragma unroll
+                    for (int j = 0; j < TB; ++j) phys[j] = plan_ids[1][j];
+                } else {
+                    fetch_ids();
+                }
                 if (kPrefetchQ && (lc.r != orow || lc.vh != ovh)) {
                     ++load_ord;
                     if (next_ord <= comp_ord) {
@@ -613,20 +737,25 @@ void decode_kernel(DecodeArgs a) {
 
         st.init();
         q_for(cc, qop, col_seq, col_hq, col_last, c);
-        fetch_ids();
+        if constexpr (MODE == kUsePlan) {
+#pragma unroll
+            for (int j = 0; j < TB; ++j) phys[j] = plan_ids[0][j];
+        } else {
+            fetch_ids();
+        }
         typename Ops::Regs ra, rb;
         // tile i is computed while tile i + 1 is in flight
-        issue(ra);
+        issue(ra, std::true_type{});
         while (true) {
             if (nloaded < ntiles) {
-                issue(rb);
+                issue(rb, std::false_type{});
                 compute(ra);
             } else {
                 compute(ra);
                 break;
             }
             if (nloaded < ntiles) {
-                issue(ra);
+                issue(ra, std::false_type{});
                 compute(rb);
             } else {
                 compute(rb);
@@ -661,7 +790,7 @@ void decode_kernel(DecodeArgs a) {
     }
 }
 
-template <int KIND, int D, int NC, bool PLAIN>
+template <int KIND, int D, int NC, bool PLAIN, int MODE = kRun>
 static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
     constexpr int NW = 4;
     int dev = 0, cus = 256;
@@ -671,7 +800,7 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     long grid = (long)cus * waves_per_simd(KIND, D);
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
-    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -686,8 +815,10 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     // tile numbers are 32-bit in the kernel
     if (tiles(16) > 0x7fffffffL) return PA_ERR_UNSUPPORTED;
 #define PA_LAUNCH(K, DD, TT)                                                          \
-    (wide ? launch_decode<K, DD, 2, false>(a, tiles(TT), stream)                      \
-          : launch_decode<K, DD, 1, true>(a, tiles(TT), stream))
+    (wide        ? launch_decode<K, DD, 2, false>(a, tiles(TT), stream)               \
+     : a.plan_out ? launch_decode<K, DD, 1, true, kMakePlan>(a, tiles(TT), stream)    \
+     : a.plan     ? launch_decode<K, DD, 1, true, kUsePlan>(a, tiles(TT), stream)     \
+                  : launch_decode<K, DD, 1, true>(a, tiles(TT), stream))
     if (kind == kBF16 && head_dim == 128) e = PA_LAUNCH(kBF16, 128, 32);
     else if (kind == kBF16 && head_dim == 64) e = PA_LAUNCH(kBF16, 64, 32);
     else if (kind == kFP8 && head_dim == 128) e = PA_LAUNCH(kFP8, 128, 64);
@@ -697,6 +828,31 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     else return PA_ERR_UNSUPPORTED;
 #undef PA_LAUNCH
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// Split-K partitions (partition_size > 0), or one item covering every
+// position a block-table row can address.
+static pa_status_t set_partitioning(DecodeArgs& a, int partition_size, int max_partitions,
+                                    int max_blocks_per_seq) {
+    if (partition_size > 0) {
+        if (partition_size % kBlock) return PA_ERR_ARG;
+        if (max_partitions < 1) return PA_ERR_ARG;
+        a.partition_size = partition_size;
+        a.max_partitions = max_partitions;
+        a.split = 1;
+    } else {
+        a.partition_size = max_blocks_per_seq * kBlock;
+        a.max_partitions = 1;
+        a.split = 0;
+    }
+    return PA_OK;
+}
+
+static long decode_grid_cap(pa_dtype_t cache_dtype, int head_dim) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return (long)cus * waves_per_simd(cache_kind(cache_dtype), head_dim);
 }
 
 // Validation and argument packing shared by pa_decode and pa_decode_cascade.
@@ -734,21 +890,9 @@ static pa_status_t pack_decode(DecodeArgs& a, void* out, const void* q, pa_dtype
     a.num_kv_heads = num_kv_heads;
     a.group = num_heads / num_kv_heads;
     a.scale_log2 = scale * kLog2e;
-    if (partition_size > 0) {
-        if (partition_size % block_size) return PA_ERR_ARG;
-        if (max_partitions < 1) return PA_ERR_ARG;
-        if (!part_max || !part_sum || !part_out) return PA_ERR_ARG;
-        a.partition_size = partition_size;
-        a.max_partitions = max_partitions;
-        a.split = 1;
-    } else {
-        if (!out) return PA_ERR_ARG;
-        // one item covers every position a block-table row can address
-        a.partition_size = max_blocks_per_seq * block_size;
-        a.max_partitions = 1;
-        a.split = 0;
-    }
-    return PA_OK;
+    if (partition_size > 0 && (!part_max || !part_sum || !part_out)) return PA_ERR_ARG;
+    if (partition_size == 0 && !out) return PA_ERR_ARG;
+    return set_partitioning(a, partition_size, max_partitions, max_blocks_per_seq);
 }
 
 }  // namespace pa
@@ -783,6 +927,7 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
                                         int32_t head_dim, int32_t block_size, float scale,
                                         int32_t partition_size, int32_t max_partitions,
                                         float* part_max, float* part_sum, float* part_out,
+                                        const int32_t* plan, size_t plan_bytes,
                                         hipStream_t stream) {
     DecodeArgs a;
     pa_status_t st = pack_decode(a, out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
@@ -798,6 +943,11 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
         a.new_slots = new_slots;
         a.k_cache_w = static_cast<char*>(k_cache);
         a.v_cache_w = static_cast<char*>(v_cache);
+    }
+    if (plan) {
+        // every word the launch may read lies inside the buffer
+        if (plan_bytes < pa_decode_plan_bytes(batch, cache_dtype, head_dim)) return PA_ERR_ARG;
+        a.plan = plan;
     }
     return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
                       false, stream);
@@ -858,4 +1008,43 @@ extern "C" pa_status_t pa_decode_multi(
     const long chunks = (max_query_len + mpv - 1) / mpv;
     return run_decode(a, cache_dtype, head_dim, (long)batch * chunks * num_kv_heads * max_partitions,
                       true, stream);
+}
+
+extern "C" size_t pa_decode_plan_bytes(int32_t batch, pa_dtype_t cache_dtype, int32_t head_dim) {
+    if (batch < 0 || batch > kMaxDecodeRows || !valid_dtype(cache_dtype)) return 0;
+    if (head_dim != 64 && head_dim != 128) return 0;
+    return (size_t)(plan_waves_offset(batch) + decode_grid_cap(cache_dtype, head_dim) * 4 * kPlanWave) *
+           sizeof(int32_t);
+}
+
+extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, pa_dtype_t cache_dtype,
+                                      int32_t partition_size, int32_t max_partitions,
+                                      hipStream_t stream) {
+    // the query dtype the cache pairs with; a plan launch reads no Q, K, V or scales
+    const pa_dtype_t q_dtype = cache_dtype == PA_DT_F32 ? PA_DT_F32 : PA_DT_BF16;
+    const float unused_scale = 1.0f;
+    pa_status_t st = check_attention_shape(q_dtype, cache_dtype, &unused_scale, &unused_scale,
+                                           num_heads, num_kv_heads, head_dim, kBlock);
+    if (st != PA_OK) return st;
+    if (batch < 0 || max_blocks_per_seq < 1 || partition_size < 0) return PA_ERR_ARG;
+    if (batch == 0) return PA_OK;
+    if (batch > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+    if (!plan || !block_tables || !context_lens) return PA_ERR_ARG;
+    if (plan_bytes < pa_decode_plan_bytes(batch, cache_dtype, head_dim)) return PA_ERR_ARG;
+    DecodeArgs a = DecodeArgs{};
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.batch = batch;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    st = set_partitioning(a, partition_size, max_partitions, max_blocks_per_seq);
+    if (st != PA_OK) return st;
+    a.plan_out = plan;
+    return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
+                      false, stream);
 }

@@ -135,12 +135,35 @@ def test_multi_query_validation():
 def test_decode_append_validation():
     lib = _lib.load()
 
-    def call(out=FAKE, kn=FAKE, vn=FAKE, sl=FAKE, ps=64, parts=FAKE, B=4):
+    def call(out=FAKE, kn=FAKE, vn=FAKE, sl=FAKE, ps=64, parts=FAKE, B=4, plan=None, nbytes=0):
         return lib.pa_decode_append(out, FAKE, 1, kn, vn, sl, FAKE, FAKE, 1, None, None, FAKE, 32,
-                                    FAKE, B, 8, 2, 128, 16, 0.1, ps, 4, parts, parts, parts, None)
+                                    FAKE, B, 8, 2, 128, 16, 0.1, ps, 4, parts, parts, parts, plan,
+                                    nbytes, None)
 
     assert call(vn=None) == _lib.PA_ERR_ARG                       # append arrays go together
     assert call(sl=None) == _lib.PA_ERR_ARG
     assert call(parts=None) == _lib.PA_ERR_ARG
     assert call(ps=0, out=None) == _lib.PA_ERR_ARG
+    assert call(plan=FAKE, nbytes=64) == _lib.PA_ERR_ARG              # plan buffer too small
     assert call(B=0) == _lib.PA_OK
+
+
+def test_decode_plan_validation():
+    lib = _lib.load()
+
+    def call(plan=FAKE, nbytes=1 << 20, B=4, hq=8, hkv=2, d=128, c_dt=1, ps=64, pmax=4):
+        return lib.pa_decode_plan(plan, nbytes, FAKE, 32, FAKE, B, hq, hkv, d, c_dt, ps, pmax, None)
+
+    assert call(plan=None) == _lib.PA_ERR_ARG
+    assert call(nbytes=64) == _lib.PA_ERR_ARG                     # smaller than the plan
+    assert call(hq=7) == _lib.PA_ERR_ARG
+    assert call(d=96) == _lib.PA_ERR_UNSUPPORTED
+    assert call(ps=24) == _lib.PA_ERR_ARG
+    assert call(B=5000) == _lib.PA_ERR_UNSUPPORTED
+    assert call(B=0, plan=None) == _lib.PA_OK
+    # header + three row arrays (16-aligned) + 16 words per wavefront of the
+    # largest grid (one workgroup of 4 per CU and wave slot)
+    assert lib.pa_decode_plan_bytes(64, 1, 128) % 64 == 0
+    assert lib.pa_decode_plan_bytes(64, 1, 64) > lib.pa_decode_plan_bytes(64, 1, 128)
+    assert lib.pa_decode_plan_bytes(-1, 1, 128) == 0
+    assert lib.pa_decode_plan_bytes(64, 1, 96) == 0

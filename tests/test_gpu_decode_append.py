@@ -133,3 +133,92 @@ def test_fused_append_ignores_a_slot_off_the_table():
     torch.cuda.synchronize()
     assert torch.equal(pool.k.view(torch.uint8), before_k.view(torch.uint8))
     assert torch.equal(pool.v.view(torch.uint8), before_v.view(torch.uint8))
+
+
+def _plan_for(w, pool, ps):
+    from paged_kv_cache_234_amd import decode_plan_buffer, pa_decode_plan
+    pmax = max(1, -(-int(np.max(w.context_lens)) // ps)) if ps else 1
+    plan = decode_plan_buffer(w.batch, pool.k, w.head_dim)
+    pa_decode_plan(plan, i32(w.block_tables), i32(w.context_lens), w.num_heads, pool.k, pool.v,
+                   partition_size=ps, max_partitions=pmax)
+    return plan
+
+
+def _run_planned(w, pool, ps, plan, out_fill=float("nan")):
+    q = w.q.contiguous()
+    B, hq, d = q.shape
+    pmax = max(1, -(-int(np.max(w.context_lens)) // ps)) if ps else 1
+    pm = torch.full((B, hq, pmax), float("nan"), device="cuda")
+    psum = torch.full_like(pm, float("nan"))
+    po = torch.full((B, hq, pmax, d), float("nan"), device="cuda")
+    out = torch.full_like(q, out_fill)
+    kw = dict(partition_size=ps, max_partitions=pmax, part_max=pm, part_sum=psum, part_out=po) \
+        if ps else {}
+    k_new, v_new, slots = decode_new_tokens(w)
+    pa_decode_append(None if ps else out, q, k_new, v_new, slots, pool.k, pool.v,
+                     i32(w.block_tables), i32(w.context_lens), w.scale, pool.k_scale, pool.v_scale,
+                     plan=plan, **kw)
+    if ps:
+        pa_decode_splitk_reduce(out, pm, psum, po, i32(w.context_lens), ps)
+    torch.cuda.synchronize()
+    return out, (pm, psum, po)
+
+
+@pytest.mark.parametrize("ps", [0, 64, 256])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_planned_launch_equals_unplanned(cache, d, ps):
+    """A launch that reads its prologue from a plan gives the pools, outputs
+    and partials of the launch that computes it, bit for bit."""
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = build_workload("fp", seed=3 * d + ps + 1, device="cuda", q_dtype=q_dtype,
+                       cache_dtype=cache, num_heads=16, num_kv_heads=2, head_dim=d,
+                       decode_lens=LENS)
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    want, parts_a = _run(w, pool_a, ps, fused=True)
+    plan = _plan_for(w, pool_b, ps)
+    got, parts_b = _run_planned(w, pool_b, ps, plan)
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
+    assert torch.equal(got, want)
+    if ps:
+        for a, b in zip(parts_a, parts_b):
+            assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
+
+
+def test_one_plan_serves_every_layer():
+    """One plan, several layers' pools (different K/V, same batch): each
+    launch equals its unplanned twin."""
+    w = build_workload("fl", seed=21, device="cuda", num_heads=16, num_kv_heads=2, head_dim=128,
+                       decode_lens=LENS * 2)
+    plan = None
+    for layer in range(3):
+        w.fill_k = (w.fill_k.float() * (1 + 0.25 * layer)).to(w.fill_k.dtype)
+        pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+        if plan is None:
+            plan = _plan_for(w, pool_b, 64)
+        want, _ = _run(w, pool_a, 64, fused=True)
+        got, _ = _run_planned(w, pool_b, 64, plan)
+        assert torch.equal(got, want)
+
+
+def test_a_plan_for_other_arguments_does_nothing():
+    """A plan made for another partition size: the launch writes nothing."""
+    w = build_workload("fw", seed=22, device="cuda", num_heads=16, num_kv_heads=2, head_dim=128,
+                       decode_lens=[100, 700, 33])
+    pool = gpu_pool(w, without_new=True)
+    before = pool.k.clone()
+    plan = _plan_for(w, pool, 64)
+    got, _ = _run_planned(w, pool, 0, plan, out_fill=3.0)
+    assert torch.all(got == 3.0)
+    assert torch.equal(pool.k.view(torch.uint8), before.view(torch.uint8))
+
+
+@pytest.mark.parametrize("cfg,ps", [(2, 256), (4, 512), (1, 0)])
+def test_planned_launch_full_size(cfg, ps):
+    w = make_config(cfg, device="cuda")
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    want, _ = _run(w, pool_a, ps, fused=True)
+    got, _ = _run_planned(w, pool_b, ps, _plan_for(w, pool_b, ps))
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(got, want)
