@@ -151,12 +151,22 @@ def main():
                 j += 1
         ridx = torch.as_tensor(rows, device=dev)
         fk, fv, fslots = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous(), i32(fslots)
-    planned = fused and not args.no_plan
-    plan = decode_plan_buffer(B, pools[0].k, d) if planned else None
+    # every decode launch reads its prologue from a plan made once per model
+    # step (the plain decode of the mixed step through pa_decode_append with
+    # no append arrays)
+    planned = not args.no_plan
+    plan = None
+    if planned:
+        plan = decode_plan_buffer(B + (len(w.prefix_groups) if cascade else 0), pools[0].k, d)
 
     def make_plan():
+        extra = {}
+        if spec:
+            extra = dict(queries=(qsl, max_q))
+        elif cascade:
+            extra = dict(groups=(g_start, g_seqs, g_plens, g_max))
         pa_decode_plan(plan, bt, lens, w.num_heads, pools[0].k, pools[0].v, partition_size=ps,
-                       max_partitions=pmax)
+                       max_partitions=pmax, **extra)
     if has_prefill:
         qp = w.q_prefill.contiguous()
         outp = torch.empty_like(qp)
@@ -201,10 +211,16 @@ def main():
                              part_out=part_out, plan=plan)
         elif spec:
             pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
-                            part_sum, part_out, pool.k_scale, pool.v_scale)
+                            part_sum, part_out, pool.k_scale, pool.v_scale, plan=plan)
         elif cascade:
             pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, g_start, g_seqs, g_plens, g_max,
-                              ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale)
+                              ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale,
+                              plan=plan)
+        elif planned:
+            pa_decode_append(out if ps == 0 else None, q, None, None, None, pool.k, pool.v, bt,
+                             lens, w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
+                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
+                             part_out=part_out, plan=plan)
         elif ps > 0:
             pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
                       partition_size=ps, max_partitions=pmax, part_max=part_max,
@@ -303,8 +319,8 @@ def main():
     copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    result_entry = ("pa_decode_append" if fused else "pa_decode_multi" if spec else
-                    "pa_decode_cascade" if cascade else "pa_decode")
+    result_entry = ("pa_decode_append" if fused or (planned and not (spec or cascade)) else
+                    "pa_decode_multi" if spec else "pa_decode_cascade" if cascade else "pa_decode")
     result = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -331,8 +347,7 @@ def main():
             "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (
-                                 "pa_decode_multi" if spec else
-                                 "pa_decode_cascade" if cascade else "pa_decode",
+                                 result_entry,
                                  " + pa_decode_splitk_reduce" if ps > 0 else "",
                                  " + pa_prefill_chunk" if has_prefill else "")),
         },

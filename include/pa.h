@@ -94,6 +94,13 @@ typedef enum {
     PA_ERR_LAUNCH = 3        /* the HIP runtime refused a launch */
 } pa_status_t;
 
+/* The decode entry point a launch plan is made for (pa_decode_plan). */
+typedef enum {
+    PA_PLAN_DECODE_APPEND = 0,   /* pa_decode_append: sequence rows */
+    PA_PLAN_DECODE_CASCADE = 1,  /* pa_decode_cascade: sequence and prefix-group rows */
+    PA_PLAN_DECODE_MULTI = 2     /* pa_decode_multi: multi-query rows */
+} pa_plan_entry_t;
+
 /*
  * Write num_tokens new K/V rows into the pools.
  *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of in_dtype
@@ -154,7 +161,8 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
  *                  in the pool (e.g. a token inside a prefix-shared block).
  *                  Any other value writes nothing.
  *                  k_new, v_new and new_slots all NULL: no append.
- *   plan           NULL, or a launch plan pa_decode_plan made for the same
+ *   plan           NULL, or a launch plan pa_decode_plan made (entry
+ *                  PA_PLAN_DECODE_APPEND) for the same
  *                  block_tables, context_lens, batch, heads, head_dim,
  *                  cache dtype, partition_size and max_partitions on this
  *                  device: the launch then skips its prologue (see
@@ -178,29 +186,41 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
                              const int32_t* plan, size_t plan_bytes, hipStream_t stream);
 
 /*
- * Launch plan for pa_decode_append.  Every layer of a decode step runs the
- * same batch: the same context lengths and block tables.  The decode
- * prologue depends only on those and the launch shape: the row table in LDS,
- * the prefix of tiles, each workgroup's and wavefront's tile range, and the
- * block ids of each wavefront's first tile.  pa_decode_plan computes it once
- * with the decode kernel's own prologue and writes it to `plan`.
- * pa_decode_append(..., plan) then reads it instead, which saves the
- * per-launch prologue and its block-id round trip for every layer.  This is
- * the plan-once, run-per-layer split that the engines the pages build on use
+ * Launch plans.  Every layer of a decode step runs the same batch: the same
+ * context lengths, block tables, prefix groups and query map.  The decode
+ * prologue depends only on those and the launch shape: the row table in
+ * LDS, the prefix of tiles, each workgroup's and wavefront's tile range, and
+ * the block ids of each wavefront's first two tiles.  pa_decode_plan
+ * computes it once, with the decode kernel's own prologue, and writes it to
+ * `plan`.  The decode entry named by `entry` then reads it when given the
+ * plan, which saves the per-launch prologue for every layer.  This is the
+ * plan-once, run-per-layer split of the engines the pages build on
  * (llm-infer, "What It Does": the decode step replayed for every layer).
- *   plan        int32 device buffer of at least pa_decode_plan_bytes(batch,
- *               cache_dtype, head_dim) bytes (the workgroup count depends on
- *               the device's compute units)
- *   other arguments as pa_decode_append (Q, K/V and scales are not read)
- * The plan stays valid while context_lens and the first ceil(L_b / 16)
- * block-table entries of every row are unchanged.  It follows the stream:
- * the plan launch must precede its users on that stream, or be otherwise
- * ordered before them.
+ *   plan        int32 device buffer of at least pa_decode_plan_bytes(rows,
+ *               cache_dtype, head_dim) bytes, rows = batch (+ num_groups for
+ *               the cascade).  The workgroup count depends on the device's
+ *               compute units.
+ *   entry       the decode entry point that will use the plan
+ *   group_*, num_groups, max_group_size   the cascade's groups (else NULL, 0)
+ *   query_start_loc, max_query_len        pa_decode_multi's query map (else
+ *                                         NULL, 0)
+ *   other arguments as that entry point (Q, K/V and scales are not read)
+ * Plans for prefix-group and multi-query rows also balance cost rather than
+ * tiles across workgroups: an item counts one extra tile, for its Q load and
+ * its partial write, so many short items weigh like a few long ones.
+ * The plan stays valid while context_lens, the first ceil(L_b / 16)
+ * block-table entries of every row, and the groups or query map are
+ * unchanged.  It follows the stream: the plan launch must precede its users
+ * on that stream, or be otherwise ordered before them.
  */
-size_t pa_decode_plan_bytes(int32_t batch, pa_dtype_t cache_dtype, int32_t head_dim);
-pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const int32_t* block_tables,
-                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+size_t pa_decode_plan_bytes(int32_t rows, pa_dtype_t cache_dtype, int32_t head_dim);
+pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_entry_t entry,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t batch,
+                           const int32_t* group_start, const int32_t* group_seqs,
+                           const int32_t* group_prefix_lens, int32_t num_groups,
+                           int32_t max_group_size, const int32_t* query_start_loc,
+                           int32_t max_query_len, int32_t num_heads, int32_t num_kv_heads,
                            int32_t head_dim, pa_dtype_t cache_dtype, int32_t partition_size,
                            int32_t max_partitions, hipStream_t stream);
 
@@ -230,6 +250,8 @@ pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const int32_t* bloc
  * batch + num_groups <= 4096 (PA_ERR_UNSUPPORTED otherwise).  num_groups == 0
  * computes exactly what pa_decode computes.
  */
+/* plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_CASCADE
+ * (see pa_decode_plan). */
 pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
                               const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
                               const float* k_scale, const float* v_scale,
@@ -242,7 +264,7 @@ pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
                               int32_t block_size, float scale,
                               int32_t partition_size, int32_t max_partitions,
                               float* part_max, float* part_sum, float* part_out,
-                              hipStream_t stream);
+                              const int32_t* plan, size_t plan_bytes, hipStream_t stream);
 
 /*
  * Multi-query split-K decode: several new query tokens per sequence, causal
@@ -267,6 +289,8 @@ pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
  *                      longer chunks are prefill: pa_prefill_chunk)
  * Requires partition_size > 0 and q_b <= L_b.
  */
+/* plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_MULTI
+ * (see pa_decode_plan). */
 pa_status_t pa_decode_multi(const void* q, pa_dtype_t q_dtype,
                             const int32_t* query_start_loc, int32_t max_query_len,
                             const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
@@ -277,7 +301,7 @@ pa_status_t pa_decode_multi(const void* q, pa_dtype_t q_dtype,
                             int32_t block_size, float scale,
                             int32_t partition_size, int32_t max_partitions,
                             float* part_max, float* part_sum, float* part_out,
-                            hipStream_t stream);
+                            const int32_t* plan, size_t plan_bytes, hipStream_t stream);
 
 /*
  * Merge split-K partials (the layout pa_decode writes) into out

@@ -50,14 +50,16 @@ def load(path=LIB_PATH):
     lib.pa_decode_append.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                      i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
                                      ctypes.c_size_t, st]
-    lib.pa_decode_plan.argtypes = [vp, ctypes.c_size_t, vp, i32, vp, i32, i32, i32, i32, i32, i32,
-                                   i32, st]
+    lib.pa_decode_plan.argtypes = [vp, ctypes.c_size_t, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
+                                   vp, i32, i32, i32, i32, i32, i32, i32, st]
     lib.pa_decode_plan_bytes.argtypes = [i32, i32, i32]
     lib.pa_decode_plan_bytes.restype = ctypes.c_size_t
     lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp,
-                                      i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
+                                      i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
+                                      ctypes.c_size_t, st]
     lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
-                                    i32, i32, i32, f32, i32, i32, vp, vp, vp, st]
+                                    i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                                    st]
     lib.pa_decode_splitk_reduce.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, st]
     lib.pa_prefill_chunk.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                                      i32, i32, i32, i32, f32, st]
@@ -136,14 +138,15 @@ def pa_decode_workspace_bytes(batch, num_heads, head_dim, max_partitions):
     return int(load().pa_decode_workspace_bytes(batch, num_heads, head_dim, max_partitions))
 
 
-def pa_decode_plan_bytes(batch, k_cache, head_dim):
-    """Bytes of a launch plan for a batch over pools of k_cache's dtype."""
-    return int(load().pa_decode_plan_bytes(int(batch), _dt(k_cache), int(head_dim)))
+def pa_decode_plan_bytes(rows, k_cache, head_dim):
+    """Bytes of a launch plan for `rows` rows (the batch, plus the prefix
+    groups for the cascade) over pools of k_cache's dtype."""
+    return int(load().pa_decode_plan_bytes(int(rows), _dt(k_cache), int(head_dim)))
 
 
-def decode_plan_buffer(batch, k_cache, head_dim, device="cuda"):
+def decode_plan_buffer(rows, k_cache, head_dim, device="cuda"):
     """An int32 device buffer large enough for pa_decode_plan."""
-    n = -(-pa_decode_plan_bytes(batch, k_cache, head_dim) // 4)
+    n = -(-pa_decode_plan_bytes(rows, k_cache, head_dim) // 4)
     return torch.empty(max(n, 1), dtype=torch.int32, device=device)
 
 
@@ -155,18 +158,39 @@ def _plan_ptr(plan):
     return _ptr(plan)
 
 
+def _plan_bytes(plan):
+    return 0 if plan is None else plan.numel() * 4
+
+
+PA_PLAN_DECODE_APPEND, PA_PLAN_DECODE_CASCADE, PA_PLAN_DECODE_MULTI = 0, 1, 2
+
+
 def pa_decode_plan(plan, block_tables, context_lens, num_heads, k_cache, v_cache, partition_size=0,
-                   max_partitions=1, stream=None):
+                   max_partitions=1, groups=None, queries=None, stream=None):
     """Fill `plan` (from decode_plan_buffer) with the decode prologue of this
-    batch, for pa_decode_append(..., plan=plan) launches with the same
-    arguments."""
+    batch for launches with the same arguments: pa_decode_append by default;
+    pa_decode_cascade with groups=(group_start, group_seqs, group_prefix_lens,
+    max_group_size); pa_decode_multi with queries=(query_start_loc,
+    max_query_len)."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     B = context_lens.numel()
     if block_tables.shape[0] != B:
         raise ValueError("inconsistent decode shapes")
-    st = load().pa_decode_plan(_plan_ptr(plan), plan.numel() * 4, _i32(block_tables, "block_tables"),
-                               block_tables.shape[1], _i32(context_lens, "context_lens"), B,
-                               int(num_heads), hkv, d, _dt(k_cache), int(partition_size),
+    entry, gs, gq, gp, ng, mg, qsl, mq = PA_PLAN_DECODE_APPEND, None, None, None, 0, 0, None, 0
+    if groups is not None:
+        entry = PA_PLAN_DECODE_CASCADE
+        gs, gq, gp, mg = groups
+        ng = gs.numel() - 1
+        gs, gq, gp = (_i32(gs, "group_start"), _i32(gq, "group_seqs"),
+                      _i32(gp, "group_prefix_lens"))
+    elif queries is not None:
+        entry = PA_PLAN_DECODE_MULTI
+        qsl, mq = queries
+        qsl = _i32(qsl, "query_start_loc")
+    st = load().pa_decode_plan(_plan_ptr(plan), _plan_bytes(plan), entry,
+                               _i32(block_tables, "block_tables"), block_tables.shape[1],
+                               _i32(context_lens, "context_lens"), B, gs, gq, gp, ng, int(mg), qsl,
+                               int(mq), int(num_heads), hkv, d, _dt(k_cache), int(partition_size),
                                int(max_partitions), _stream(stream))
     _check("pa_decode_plan", st)
 
@@ -249,15 +273,15 @@ def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_ta
                                  block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,
                                  hkv, d, bs, float(scale), int(partition_size),
                                  int(max_partitions), _ptr(part_max), _ptr(part_sum),
-                                 _ptr(part_out), _plan_ptr(plan),
-                                 0 if plan is None else plan.numel() * 4, _stream(stream))
+                                 _ptr(part_out), _plan_ptr(plan), _plan_bytes(plan),
+                                 _stream(stream))
     _check("pa_decode_append", st)
 
 
 def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, group_start,
                       group_seqs, group_prefix_lens, max_group_size, partition_size,
                       max_partitions, part_max, part_sum, part_out, k_scale=None, v_scale=None,
-                      stream=None):
+                      plan=None, stream=None):
     """Split-K partials like pa_decode, reading each prefix group's shared
     partitions once for up to 16/G members at a time.  group_start int32
     [num_groups + 1], group_seqs int32 [members], group_prefix_lens int32
@@ -284,13 +308,14 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, gr
                                   _i32(group_prefix_lens, "group_prefix_lens"), ng,
                                   int(max_group_size), hq, hkv, d, bs, float(scale),
                                   int(partition_size), int(max_partitions), _ptr(part_max),
-                                  _ptr(part_sum), _ptr(part_out), _stream(stream))
+                                  _ptr(part_sum), _ptr(part_out), _plan_ptr(plan),
+                                  _plan_bytes(plan), _stream(stream))
     _check("pa_decode_cascade", st)
 
 
 def pa_decode_multi(q, query_start_loc, max_query_len, k_cache, v_cache, block_tables,
                     context_lens, scale, partition_size, max_partitions, part_max, part_sum,
-                    part_out, k_scale=None, v_scale=None, stream=None):
+                    part_out, k_scale=None, v_scale=None, plan=None, stream=None):
     """Split-K partials for q_b causal query tokens per sequence: q [T, Hq, D]
     with T = query_start_loc[-1]; partials [T, Hq, max_partitions] (+ [D])."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
@@ -311,7 +336,8 @@ def pa_decode_multi(q, query_start_loc, max_query_len, k_cache, v_cache, block_t
                                 _ptr(k_scale), _ptr(v_scale), _i32(block_tables, "block_tables"),
                                 block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,
                                 hkv, d, bs, float(scale), int(partition_size), int(max_partitions),
-                                _ptr(part_max), _ptr(part_sum), _ptr(part_out), _stream(stream))
+                                _ptr(part_max), _ptr(part_sum), _ptr(part_out), _plan_ptr(plan),
+                                _plan_bytes(plan), _stream(stream))
     _check("pa_decode_multi", st)
 
 

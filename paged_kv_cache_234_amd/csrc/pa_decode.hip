@@ -48,9 +48,10 @@ constexpr int kMaxMultiQuery = 64;     // query tokens per sequence in pa_decode
 // lengths, the block tables and the launch shape, which every layer of a
 // decode step shares.  A plan holds it as int32 words:
 //   [0, 16)             header (kPlan* fields below)
-//   [16, 16 + B)        context length per row (cut as the prologue cuts it)
-//   [16 + B, 16 + 2B)   tiles per KV head per row
-//   [16 + 2B, 17 + 3B)  exclusive prefix of tiles (B + 1 entries)
+//   [16, 16 + R)        context length per row (cut as the prologue cuts it)
+//   [16 + R, 16 + 2R)   the row's aux word (plain rows: tiles per KV head)
+//   [16 + 2R, 17 + 3R)  exclusive prefix of tiles (R + 1 entries)
+// for R rows (the sequences, then any prefix groups).
 //   then, 16-aligned, 16 words per wavefront (grid x 4): first and end tile,
 //   its workgroup's first and end tile, the rows of its first and last tile,
 //   the block ids of its first tile (4 words) and of its second (4 words).
@@ -58,7 +59,8 @@ enum { kRun = 0, kMakePlan = 1, kUsePlan = 2 };
 constexpr int kPlanMagic = 0x50414450;
 enum {
     kPlanMagicW, kPlanBatch, kPlanKvHeads, kPlanPS, kPlanMaxPart, kPlanTT, kPlanGrid, kPlanNW,
-    kPlanMaxBlocks, kPlanSplit, kPlanTiles, kPlanHeadDim, kPlanHeader = 16
+    kPlanMaxBlocks, kPlanSplit, kPlanTiles, kPlanHeadDim, kPlanRows, kPlanRowKind,
+    kPlanHeader = 16
 };
 constexpr int kPlanWave = 16;
 __host__ __device__ constexpr long plan_waves_offset(int batch) {
@@ -120,6 +122,12 @@ template <int NVT, int NC> struct SegSlot {
     float m[NC][kWave], mr[NC][kWave], l[NC][kWave];
 };
 
+// Group and multi-query rows balance cost, not tiles, in the ranges a plan
+// records: an item costs its tiles plus kWideItemCost (its Q load, its
+// partial write and the cursor's turn), so many short items weigh like the
+// long ones they stand beside.
+constexpr int kWideItemCost = 1;
+
 // NC: 16-column query tiles per wavefront.  Sequence rows use one (their
 // columns are one KV head's G <= 16 query heads); group and multi-query rows
 // give each virtual head NC * 16 columns, so one K/V tile feeds up to
@@ -129,7 +137,8 @@ template <int NVT, int NC> struct SegSlot {
 template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
-    static_assert(PLAIN || MODE == kRun, "plans cover plain decode only");
+    // which rows a plan describes: plain sequences, cascade or multi-query
+    const int row_kind = PLAIN ? 0 : (a.query_start_loc != nullptr ? 2 : 1);
     using Ops = TileOps<KIND, D>;
     using QT = typename QType<KIND>::T;
     constexpr int TT = Ops::TT, TB = Ops::TB, NVT = Ops::NVT, ELEM = Ops::ELEM;
@@ -142,6 +151,13 @@ void decode_kernel(DecodeArgs a) {
     __shared__ int s_aux[kMaxDecodeRows];
     __shared__ int s_tpre[kMaxDecodeRows + 1];
     __shared__ int s_wsum[NW];
+    // a plan for group or multi-query rows balances cost (kWideItemCost);
+    // exclusive prefix of that cost per row
+    constexpr bool kCost = !PLAIN && MODE == kMakePlan;
+    constexpr int kItemCost = kCost ? kWideItemCost : 0;
+    __shared__ int s_cpre[kCost ? kMaxDecodeRows + 1 : 1];
+    __shared__ int s_csum[NW];
+    __shared__ int s_wstart[NW + 1];             // the wavefronts' first tiles, then the end
     __shared__ SegSlot<NVT, NC> s_seg[NW];       // each wave's first piece, if cut
 
     const int tid = threadIdx.x;
@@ -168,6 +184,7 @@ void decode_kernel(DecodeArgs a) {
         const int eff_ps = PS, eff_mp = a.max_partitions;
         plan_ok = load_invariant(pl + kPlanMagicW) == kPlanMagic &&
                   load_invariant(pl + kPlanBatch) == B && load_invariant(pl + kPlanKvHeads) == Hkv &&
+                  load_invariant(pl + kPlanRows) == R && load_invariant(pl + kPlanRowKind) == row_kind &&
                   load_invariant(pl + kPlanPS) == eff_ps &&
                   load_invariant(pl + kPlanMaxPart) == eff_mp &&
                   load_invariant(pl + kPlanTT) == TT &&
@@ -176,7 +193,7 @@ void decode_kernel(DecodeArgs a) {
                   load_invariant(pl + kPlanMaxBlocks) == a.max_blocks_per_seq &&
                   load_invariant(pl + kPlanSplit) == a.split &&
                   load_invariant(pl + kPlanHeadDim) == D;
-        const int32_t* wv = pl + plan_waves_offset(B) + ((long)blockIdx.x * NW + wave) * kPlanWave;
+        const int32_t* wv = pl + plan_waves_offset(R) + ((long)blockIdx.x * NW + wave) * kPlanWave;
         T = load_invariant(pl + kPlanTiles);
         g0 = load_invariant(wv + 0);
         g1 = load_invariant(wv + 1);
@@ -189,12 +206,12 @@ void decode_kernel(DecodeArgs a) {
             plan_ids[0][j] = load_invariant(wv + 6 + j);
             plan_ids[1][j] = load_invariant(wv + 10 + j);
         }
-        for (int r = tid; r < B; r += NT) {
+        for (int r = tid; r < R; r += NT) {
             s_len[r] = pl[kPlanHeader + r];
-            s_aux[r] = pl[kPlanHeader + B + r];
-            s_tpre[r] = pl[kPlanHeader + 2 * B + r];
+            s_aux[r] = pl[kPlanHeader + R + r];
+            s_tpre[r] = pl[kPlanHeader + 2 * R + r];
         }
-        if (tid == 0) s_tpre[B] = pl[kPlanHeader + 3 * B];
+        if (tid == 0) s_tpre[R] = pl[kPlanHeader + 3 * R];
         if (!plan_ok) g0 = g1 = wg_a = wg_e = 0;
     } else {
     // ---- row table in LDS -------------------------------------------------------
@@ -283,35 +300,53 @@ void decode_kernel(DecodeArgs a) {
     // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
     const int per = (R + NT - 1) / NT;
     const int r0 = tid * per;
-    int local = 0;
+    auto row_cost = [&](int r) { return row_heads(r) * (head_tiles_of(r) + kItemCost * row_items(r)); };
+    int local = 0, local_c = 0;
     for (int k = 0; k < per; ++k)
         if (r0 + k < R) {
             const int th = head_tiles_of(r0 + k);
             if (PLAIN) s_aux[r0 + k] = th;
             local += row_heads(r0 + k) * th;
+            if (kCost) local_c += row_cost(r0 + k);
         }
-    int incl = local;                                     // inclusive scan within the wave
+    int incl = local, incl_c = local_c;                  // inclusive scans within the wave
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int u = __shfl_up(incl, off);
-        if (lane >= off) incl += u;
+        const int uc = kCost ? __shfl_up(incl_c, off) : 0;
+        if (lane >= off) {
+            incl += u;
+            incl_c += uc;
+        }
     }
-    if (lane == kWave - 1) s_wsum[wave] = incl;
+    if (lane == kWave - 1) {
+        s_wsum[wave] = incl;
+        s_csum[wave] = incl_c;
+    }
     __syncthreads();
-    int wbase = 0, total_tiles = 0;
+    int wbase = 0, total_tiles = 0, cbase = 0, total_cost = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         wbase += (w < wave) ? s_wsum[w] : 0;
         total_tiles += s_wsum[w];
+        cbase += (w < wave) ? s_csum[w] : 0;
+        total_cost += s_csum[w];
     }
     {
-        int run = wbase + incl - local;
+        int run = wbase + incl - local, run_c = cbase + incl_c - local_c;
         for (int k = 0; k < per; ++k)
             if (r0 + k < R) {
                 s_tpre[r0 + k] = run;
                 run += row_heads(r0 + k) * (PLAIN ? s_aux[r0 + k] : head_tiles_of(r0 + k));
+                if (kCost) {
+                    s_cpre[r0 + k] = run_c;
+                    run_c += row_cost(r0 + k);
+                }
             }
-        if (tid == 0) s_tpre[R] = total_tiles;
+        if (tid == 0) {
+            s_tpre[R] = total_tiles;
+            if (kCost) s_cpre[R] = total_cost;
+        }
     }
     if constexpr (MODE == kRun) zero_empty_rows();
     __syncthreads();
@@ -326,13 +361,13 @@ void decode_kernel(DecodeArgs a) {
     // candidates at a time (two LDS round trips for 4096 rows).  tpre is
     // nondecreasing, so the lanes whose candidate qualifies form a prefix of
     // the wave.
-    auto row_of2 = [&](int ga, int gb, int& ra, int& rb) {
+    auto row_of2_in = [&](const int* pre, int ga, int gb, int& ra, int& rb) {
         int loa = 0, spa = R, lob = 0, spb = R;
         while (spa > 1 || spb > 1) {
             const int sta = (spa + kWave - 1) / kWave, stb = (spb + kWave - 1) / kWave;
             const int ia = loa + lane * sta, ib = lob + lane * stb;
-            const bool oka = spa > 1 && ia < loa + spa && s_tpre[ia] <= ga;
-            const bool okb = spb > 1 && ib < lob + spb && s_tpre[ib] <= gb;
+            const bool oka = spa > 1 && ia < loa + spa && pre[ia] <= ga;
+            const bool okb = spb > 1 && ib < lob + spb && pre[ib] <= gb;
             const int ca = __builtin_popcountll(__builtin_amdgcn_ballot_w64(oka));
             const int cb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(okb));
             if (spa > 1) {
@@ -349,6 +384,7 @@ void decode_kernel(DecodeArgs a) {
         ra = loa;
         rb = lob;
     };
+    auto row_of2 = [&](int ga, int gb, int& ra, int& rb) { row_of2_in(s_tpre, ga, gb, ra, rb); };
     // the item start nearest to tile g < T in row r (the earlier one on a tie)
     auto nearest_item_start = [&](int g, int r) -> int {
         const int th = row_head_tiles(r);
@@ -360,22 +396,88 @@ void decode_kernel(DecodeArgs a) {
         const int after = p + 1 < row_items(r) ? before + tpi : head0 + th;
         return (g - before <= after - g) ? before : after;
     };
-    // T k / NWG, exact: the double product is below 2^53 and a non-integral
-    // quotient stays at least 1 / (T k) away from the next integer
-    auto share = [&](int k) { return (int)((double)T * k / (double)gridDim.x); };
-    const int sa = share(blockIdx.x), se = share(blockIdx.x + 1);
-    if (T > 0) {
-        int rsa, rse;
-        row_of2(min(sa, T - 1), min(se, T - 1), rsa, rse);
-        wg_a = sa >= T ? T : nearest_item_start(sa, rsa);
-        wg_e = se >= T ? T : nearest_item_start(se, rse);
+    // X k / NWG, exact: the double product is below 2^53 and a non-integral
+    // quotient stays at least 1 / (X k) away from the next integer
+    auto share = [&](int x, int k) { return (int)((double)x * k / (double)gridDim.x); };
+    if constexpr (!kCost) {
+        const int sa = share(T, blockIdx.x), se = share(T, blockIdx.x + 1);
+        if (T > 0) {
+            int rsa, rse;
+            row_of2(min(sa, T - 1), min(se, T - 1), rsa, rse);
+            wg_a = sa >= T ? T : nearest_item_start(sa, rsa);
+            wg_e = se >= T ? T : nearest_item_start(se, rse);
+        }
+        g0 = wg_a + (wg_e - wg_a) * wave / NW;
+        g1 = wg_a + (wg_e - wg_a) * (wave + 1) / NW;
+    } else {
+        // the same on cost: workgroup k takes the items between the item
+        // starts nearest to costs C k / NWG and C (k+1) / NWG, and its
+        // wavefronts split that run into equal costs (at tile granularity)
+        const int C = total_cost;
+        const int ci = tpi + kItemCost;                   // cost of a full item
+        struct HeadAt {
+            int tile0, cost0, th, n, o, p;                // head's first tile / cost; offset o
+        };
+        auto head_at = [&](int c, int r) {                // the (virtual) head of row r holding cost c
+            HeadAt h;
+            h.th = head_tiles_of(r);
+            h.n = row_items(r);
+            const int ch = h.th + kItemCost * h.n;
+            const int vh = (c - s_cpre[r]) / ch;
+            h.tile0 = s_tpre[r] + vh * h.th;
+            h.cost0 = s_cpre[r] + vh * ch;
+            h.o = c - h.cost0;
+            h.p = min(h.o / ci, h.n - 1);
+            return h;
+        };
+        auto nearest_item_by_cost = [&](int c, int r, int& tile, int& cost) {
+            const HeadAt h = head_at(c, r);
+            const int before = h.p * ci;
+            const bool last = h.p + 1 == h.n;
+            const int after = last ? h.th + kItemCost * h.n : before + ci;
+            const bool take_before = h.o - before <= after - h.o;
+            tile = h.tile0 + (take_before ? h.p * tpi : (last ? h.th : (h.p + 1) * tpi));
+            cost = h.cost0 + (take_before ? before : after);
+        };
+        auto tile_at_cost = [&](int c, int r) {           // inside an item, or its successor's start
+            const HeadAt h = head_at(c, r);
+            const int nt = h.p + 1 < h.n ? tpi : h.th - h.p * tpi;
+            return h.tile0 + h.p * tpi + min(h.o - h.p * ci, nt);
+        };
+        int ca = 0, ce = 0;
+        const int sa = share(C, blockIdx.x), se = share(C, blockIdx.x + 1);
+        if (C > 0) {
+            int rsa, rse;
+            row_of2_in(s_cpre, min(sa, C - 1), min(se, C - 1), rsa, rse);
+            if (sa >= C) {
+                wg_a = T;
+                ca = C;
+            } else {
+                nearest_item_by_cost(sa, rsa, wg_a, ca);
+            }
+            if (se >= C) {
+                wg_e = T;
+                ce = C;
+            } else {
+                nearest_item_by_cost(se, rse, wg_e, ce);
+            }
+        }
+        g0 = g1 = wg_a;
+        if (ce > ca) {
+            const int cw0 = ca + (ce - ca) * wave / NW, cw1 = ca + (ce - ca) * (wave + 1) / NW;
+            int rc0, rc1;
+            row_of2_in(s_cpre, min(cw0, C - 1), min(cw1, C - 1), rc0, rc1);
+            g0 = cw0 >= ce ? wg_e : tile_at_cost(cw0, rc0);
+            g1 = cw1 >= ce ? wg_e : tile_at_cost(cw1, rc1);
+        }
     }
-    g0 = wg_a + (wg_e - wg_a) * wave / NW;
-    g1 = wg_a + (wg_e - wg_a) * (wave + 1) / NW;
     // rows of this wavefront's first and last tiles
     if (g1 > g0) row_of2(g0, g1 - 1, rg0, rg1);
     }
-    auto wave_start = [&](int w) { return wg_a + (wg_e - wg_a) * w / NW; };
+    // each wavefront's first tile (and the workgroup's end), for the merge
+    s_wstart[wave] = g0;
+    if (wave == NW - 1) s_wstart[NW] = g1;
+    auto wave_start = [&](int w) { return s_wstart[w]; };
     const int ntiles = g1 - g0;
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
@@ -482,11 +584,11 @@ void decode_kernel(DecodeArgs a) {
     // ---- plan launch: record what this prologue found, then stop ----------
     if constexpr (MODE == kMakePlan) {
         int32_t* pl = a.plan_out;
-        int32_t* wv = pl + plan_waves_offset(B) + ((long)blockIdx.x * NW + wave) * kPlanWave;
+        int32_t* wv = pl + plan_waves_offset(R) + ((long)blockIdx.x * NW + wave) * kPlanWave;
         int w = 0;
         // block ids of the first two tiles, as the load cursor would fetch them
         auto tile_ids = [&](const Cursor& c, int at) {
-            const int32_t* btr = a.block_tables + (long)c.r * a.max_blocks_per_seq;
+            const int32_t* btr = a.block_tables + (long)table_seq(c.r) * a.max_blocks_per_seq;
             const int lb = (c.tb + c.jj * TT) / kBlock, last = (c.te - 1) / kBlock;
             if (lane >= at && lane < at + TB) w = btr[min(lb + lane - at, last)];
         };
@@ -502,22 +604,22 @@ void decode_kernel(DecodeArgs a) {
             if (lane == k) w = vals[k];
         if (lane < kPlanWave) wv[lane] = w;
         if (blockIdx.x == 0) {
-            for (int r = tid; r < B; r += NT) {
+            for (int r = tid; r < R; r += NT) {
                 pl[kPlanHeader + r] = s_len[r];
-                pl[kPlanHeader + B + r] = s_aux[r];
-                pl[kPlanHeader + 2 * B + r] = s_tpre[r];
+                pl[kPlanHeader + R + r] = s_aux[r];
+                pl[kPlanHeader + 2 * R + r] = s_tpre[r];
             }
             if (tid < kPlanHeader) {
                 const int hdr[kPlanHeader] = {kPlanMagic, B, Hkv, PS, a.max_partitions, TT,
                                               (int)gridDim.x, NW, a.max_blocks_per_seq, a.split,
-                                              T, D, 0, 0, 0, 0};
+                                              T, D, R, row_kind, 0, 0};
                 int v = 0;
 #pragma unroll
                 for (int k = 0; k < kPlanHeader; ++k)
                     if (tid == k) v = hdr[k];
                 pl[tid] = v;
             }
-            if (tid == 0) pl[kPlanHeader + 3 * B] = T;
+            if (tid == 0) pl[kPlanHeader + 3 * R] = T;
         }
         return;
     }
@@ -815,10 +917,12 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     // tile numbers are 32-bit in the kernel
     if (tiles(16) > 0x7fffffffL) return PA_ERR_UNSUPPORTED;
 #define PA_LAUNCH(K, DD, TT)                                                          \
-    (wide        ? launch_decode<K, DD, 2, false>(a, tiles(TT), stream)               \
-     : a.plan_out ? launch_decode<K, DD, 1, true, kMakePlan>(a, tiles(TT), stream)    \
-     : a.plan     ? launch_decode<K, DD, 1, true, kUsePlan>(a, tiles(TT), stream)     \
-                  : launch_decode<K, DD, 1, true>(a, tiles(TT), stream))
+    (wide ? (a.plan_out ? launch_decode<K, DD, 2, false, kMakePlan>(a, tiles(TT), stream) \
+             : a.plan   ? launch_decode<K, DD, 2, false, kUsePlan>(a, tiles(TT), stream)  \
+                        : launch_decode<K, DD, 2, false>(a, tiles(TT), stream))           \
+          : (a.plan_out ? launch_decode<K, DD, 1, true, kMakePlan>(a, tiles(TT), stream)  \
+             : a.plan   ? launch_decode<K, DD, 1, true, kUsePlan>(a, tiles(TT), stream)   \
+                        : launch_decode<K, DD, 1, true>(a, tiles(TT), stream)))
     if (kind == kBF16 && head_dim == 128) e = PA_LAUNCH(kBF16, 128, 32);
     else if (kind == kBF16 && head_dim == 64) e = PA_LAUNCH(kBF16, 64, 32);
     else if (kind == kFP8 && head_dim == 128) e = PA_LAUNCH(kFP8, 128, 64);
@@ -895,6 +999,43 @@ static pa_status_t pack_decode(DecodeArgs& a, void* out, const void* q, pa_dtype
     return set_partitioning(a, partition_size, max_partitions, max_blocks_per_seq);
 }
 
+// Cascade rows: validation, the group fields and the item bound the grid is
+// sized by (batch > 0).
+static pa_status_t set_cascade(DecodeArgs& a, const int32_t* group_start, const int32_t* group_seqs,
+                               const int32_t* group_prefix_lens, int num_groups,
+                               int max_group_size, long& items) {
+    if (num_groups < 0 || max_group_size < 0 || max_group_size > 0xFFFF) return PA_ERR_ARG;
+    if (num_groups > 0 && (!group_start || !group_seqs || !group_prefix_lens)) return PA_ERR_ARG;
+    if ((long)a.batch + num_groups > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
+    a.group_start = group_start;
+    a.group_seqs = group_seqs;
+    a.group_prefix_lens = group_prefix_lens;
+    a.num_groups = num_groups;
+    const int mpv = 2 * (16 / a.group);                       // members per virtual head
+    const long chunks = (max_group_size + mpv - 1) / mpv;
+    items = ((long)a.batch + (long)num_groups * chunks) * a.num_kv_heads * a.max_partitions;
+    return PA_OK;
+}
+
+// Multi-query rows: validation, the query map and the item bound (batch > 0;
+// `none` when no sequence has a query token).
+static pa_status_t set_multi(DecodeArgs& a, const int32_t* query_start_loc, int max_query_len,
+                             long& items, bool& none) {
+    if (max_query_len < 0) return PA_ERR_ARG;
+    if (max_query_len > kMaxMultiQuery) return PA_ERR_UNSUPPORTED;
+    none = max_query_len == 0;
+    if (none) return PA_OK;
+    if (!query_start_loc) return PA_ERR_ARG;
+    a.query_start_loc = query_start_loc;
+    const int mpv = 2 * (16 / a.group);                       // query tokens per virtual head
+    const long chunks = (max_query_len + mpv - 1) / mpv;
+    items = (long)a.batch * chunks * a.num_kv_heads * a.max_partitions;
+    return PA_OK;
+}
+
+// A plan buffer for `rows` rows large enough for every word a launch reads.
+static bool plan_fits(size_t plan_bytes, int rows, pa_dtype_t cache_dtype, int head_dim);
+
 }  // namespace pa
 
 using namespace pa;
@@ -946,7 +1087,7 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
     }
     if (plan) {
         // every word the launch may read lies inside the buffer
-        if (plan_bytes < pa_decode_plan_bytes(batch, cache_dtype, head_dim)) return PA_ERR_ARG;
+        if (!plan_fits(plan_bytes, batch, cache_dtype, head_dim)) return PA_ERR_ARG;
         a.plan = plan;
     }
     return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
@@ -961,7 +1102,7 @@ extern "C" pa_status_t pa_decode_cascade(
     const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_size,
     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
     int32_t partition_size, int32_t max_partitions, float* part_max, float* part_sum,
-    float* part_out, hipStream_t stream) {
+    float* part_out, const int32_t* plan, size_t plan_bytes, hipStream_t stream) {
     if (partition_size <= 0) return PA_ERR_ARG;
     DecodeArgs a;
     pa_status_t st = pack_decode(a, nullptr, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
@@ -973,15 +1114,14 @@ extern "C" pa_status_t pa_decode_cascade(
     if (num_groups > 0 && (!group_start || !group_seqs || !group_prefix_lens)) return PA_ERR_ARG;
     if ((long)batch + num_groups > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
     if (batch == 0) return PA_OK;
-    a.group_start = group_start;
-    a.group_seqs = group_seqs;
-    a.group_prefix_lens = group_prefix_lens;
-    a.num_groups = num_groups;
-    const int mpv = 2 * (16 / (num_heads / num_kv_heads));   // members per virtual head
-    const long chunks = (max_group_size + mpv - 1) / mpv;
-    const long rows_bound = (long)batch + (long)num_groups * chunks;
-    return run_decode(a, cache_dtype, head_dim, rows_bound * num_kv_heads * max_partitions, true,
-                      stream);
+    long items = 0;
+    st = set_cascade(a, group_start, group_seqs, group_prefix_lens, num_groups, max_group_size, items);
+    if (st != PA_OK) return st;
+    if (plan) {
+        if (!plan_fits(plan_bytes, batch + num_groups, cache_dtype, head_dim)) return PA_ERR_ARG;
+        a.plan = plan;
+    }
+    return run_decode(a, cache_dtype, head_dim, items, true, stream);
 }
 
 extern "C" pa_status_t pa_decode_multi(
@@ -991,7 +1131,7 @@ extern "C" pa_status_t pa_decode_multi(
     const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float scale, int32_t partition_size,
     int32_t max_partitions, float* part_max, float* part_sum, float* part_out,
-    hipStream_t stream) {
+    const int32_t* plan, size_t plan_bytes, hipStream_t stream) {
     if (partition_size <= 0) return PA_ERR_ARG;
     DecodeArgs a;
     pa_status_t st = pack_decode(a, nullptr, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
@@ -1002,27 +1142,44 @@ extern "C" pa_status_t pa_decode_multi(
     if (max_query_len < 0) return PA_ERR_ARG;
     if (max_query_len > kMaxMultiQuery) return PA_ERR_UNSUPPORTED;
     if (batch == 0 || max_query_len == 0) return PA_OK;
-    if (!query_start_loc) return PA_ERR_ARG;
-    a.query_start_loc = query_start_loc;
-    const int mpv = 2 * (16 / (num_heads / num_kv_heads));   // query tokens per virtual head
-    const long chunks = (max_query_len + mpv - 1) / mpv;
-    return run_decode(a, cache_dtype, head_dim, (long)batch * chunks * num_kv_heads * max_partitions,
-                      true, stream);
+    long items = 0;
+    bool none = false;
+    st = set_multi(a, query_start_loc, max_query_len, items, none);
+    if (st != PA_OK || none) return st;
+    if (plan) {
+        if (!plan_fits(plan_bytes, batch, cache_dtype, head_dim)) return PA_ERR_ARG;
+        a.plan = plan;
+    }
+    return run_decode(a, cache_dtype, head_dim, items, true, stream);
 }
 
-extern "C" size_t pa_decode_plan_bytes(int32_t batch, pa_dtype_t cache_dtype, int32_t head_dim) {
-    if (batch < 0 || batch > kMaxDecodeRows || !valid_dtype(cache_dtype)) return 0;
+extern "C" size_t pa_decode_plan_bytes(int32_t rows, pa_dtype_t cache_dtype, int32_t head_dim) {
+    if (rows < 0 || rows > kMaxDecodeRows || !valid_dtype(cache_dtype)) return 0;
     if (head_dim != 64 && head_dim != 128) return 0;
-    return (size_t)(plan_waves_offset(batch) + decode_grid_cap(cache_dtype, head_dim) * 4 * kPlanWave) *
+    return (size_t)(plan_waves_offset(rows) + decode_grid_cap(cache_dtype, head_dim) * 4 * kPlanWave) *
            sizeof(int32_t);
 }
 
-extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                      int32_t batch, int32_t num_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, pa_dtype_t cache_dtype,
-                                      int32_t partition_size, int32_t max_partitions,
-                                      hipStream_t stream) {
+namespace pa {
+static bool plan_fits(size_t plan_bytes, int rows, pa_dtype_t cache_dtype, int head_dim) {
+    const size_t need = pa_decode_plan_bytes(rows, cache_dtype, head_dim);
+    return need > 0 && plan_bytes >= need;
+}
+}  // namespace pa
+
+extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_entry_t entry,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t batch,
+                                      const int32_t* group_start, const int32_t* group_seqs,
+                                      const int32_t* group_prefix_lens, int32_t num_groups,
+                                      int32_t max_group_size, const int32_t* query_start_loc,
+                                      int32_t max_query_len, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      pa_dtype_t cache_dtype, int32_t partition_size,
+                                      int32_t max_partitions, hipStream_t stream) {
+    if (entry != PA_PLAN_DECODE_APPEND && entry != PA_PLAN_DECODE_CASCADE &&
+        entry != PA_PLAN_DECODE_MULTI)
+        return PA_ERR_ARG;
     // the query dtype the cache pairs with; a plan launch reads no Q, K, V or scales
     const pa_dtype_t q_dtype = cache_dtype == PA_DT_F32 ? PA_DT_F32 : PA_DT_BF16;
     const float unused_scale = 1.0f;
@@ -1030,10 +1187,11 @@ extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const in
                                            num_heads, num_kv_heads, head_dim, kBlock);
     if (st != PA_OK) return st;
     if (batch < 0 || max_blocks_per_seq < 1 || partition_size < 0) return PA_ERR_ARG;
+    if (entry != PA_PLAN_DECODE_APPEND && partition_size == 0) return PA_ERR_ARG;
+    if (entry == PA_PLAN_DECODE_CASCADE && num_groups < 0) return PA_ERR_ARG;
     if (batch == 0) return PA_OK;
     if (batch > kMaxDecodeRows) return PA_ERR_UNSUPPORTED;
     if (!plan || !block_tables || !context_lens) return PA_ERR_ARG;
-    if (plan_bytes < pa_decode_plan_bytes(batch, cache_dtype, head_dim)) return PA_ERR_ARG;
     DecodeArgs a = DecodeArgs{};
     a.block_tables = block_tables;
     a.context_lens = context_lens;
@@ -1044,7 +1202,19 @@ extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, const in
     a.group = num_heads / num_kv_heads;
     st = set_partitioning(a, partition_size, max_partitions, max_blocks_per_seq);
     if (st != PA_OK) return st;
+    long items = (long)batch * num_kv_heads * a.max_partitions;
+    int rows = batch;
+    if (entry == PA_PLAN_DECODE_CASCADE) {
+        st = set_cascade(a, group_start, group_seqs, group_prefix_lens, num_groups, max_group_size,
+                         items);
+        rows = batch + num_groups;
+    } else if (entry == PA_PLAN_DECODE_MULTI) {
+        bool none = false;
+        st = set_multi(a, query_start_loc, max_query_len, items, none);
+        if (st == PA_OK && none) return PA_OK;            // no launch will read it
+    }
+    if (st != PA_OK) return st;
+    if (!plan_fits(plan_bytes, rows, cache_dtype, head_dim)) return PA_ERR_ARG;
     a.plan_out = plan;
-    return run_decode(a, cache_dtype, head_dim, (long)batch * num_kv_heads * a.max_partitions,
-                      false, stream);
+    return run_decode(a, cache_dtype, head_dim, items, entry != PA_PLAN_DECODE_APPEND, stream);
 }

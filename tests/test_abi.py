@@ -102,10 +102,11 @@ def test_append_reduce_prefill_validation():
 def test_cascade_validation():
     lib = _lib.load()
 
-    def call(ps=256, pmax=4, B=4, ng=1, mgs=4, gs=FAKE, gq=FAKE, gp=FAKE, parts=FAKE):
+    def call(ps=256, pmax=4, B=4, ng=1, mgs=4, gs=FAKE, gq=FAKE, gp=FAKE, parts=FAKE, plan=None,
+             nbytes=0):
         return lib.pa_decode_cascade(FAKE, 1, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B, gs,
                                      gq, gp, ng, mgs, 8, 2, 128, 16, 0.1, ps, pmax, parts, parts,
-                                     parts, None)
+                                     parts, plan, nbytes, None)
 
     assert call(ps=0) == _lib.PA_ERR_ARG                         # split-K only
     assert call(parts=None) == _lib.PA_ERR_ARG                   # partial buffers required
@@ -113,15 +114,17 @@ def test_cascade_validation():
     assert call(ng=-1) == _lib.PA_ERR_ARG
     assert call(mgs=-1) == _lib.PA_ERR_ARG
     assert call(B=4000, ng=200) == _lib.PA_ERR_UNSUPPORTED       # more than 4096 rows
+    assert call(plan=FAKE, nbytes=64) == _lib.PA_ERR_ARG          # plan buffer too small
     assert call(B=0) == _lib.PA_OK
 
 
 def test_multi_query_validation():
     lib = _lib.load()
 
-    def call(ps=64, pmax=4, B=4, mq=8, qsl=FAKE, parts=FAKE):
+    def call(ps=64, pmax=4, B=4, mq=8, qsl=FAKE, parts=FAKE, plan=None, nbytes=0):
         return lib.pa_decode_multi(FAKE, 1, qsl, mq, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B,
-                                   8, 2, 128, 16, 0.1, ps, pmax, parts, parts, parts, None)
+                                   8, 2, 128, 16, 0.1, ps, pmax, parts, parts, parts, plan,
+                                   nbytes, None)
 
     assert call(ps=0) == _lib.PA_ERR_ARG
     assert call(parts=None) == _lib.PA_ERR_ARG
@@ -151,10 +154,18 @@ def test_decode_append_validation():
 def test_decode_plan_validation():
     lib = _lib.load()
 
-    def call(plan=FAKE, nbytes=1 << 20, B=4, hq=8, hkv=2, d=128, c_dt=1, ps=64, pmax=4):
-        return lib.pa_decode_plan(plan, nbytes, FAKE, 32, FAKE, B, hq, hkv, d, c_dt, ps, pmax, None)
+    def call(plan=FAKE, nbytes=1 << 20, entry=0, B=4, hq=8, hkv=2, d=128, c_dt=1, ps=64, pmax=4,
+             gs=None, ng=0, qsl=None, mq=0):
+        return lib.pa_decode_plan(plan, nbytes, entry, FAKE, 32, FAKE, B, gs, gs, gs, ng, 4, qsl,
+                                  mq, hq, hkv, d, c_dt, ps, pmax, None)
 
     assert call(plan=None) == _lib.PA_ERR_ARG
+    assert call(entry=3) == _lib.PA_ERR_ARG
+    assert call(entry=1, ng=2) == _lib.PA_ERR_ARG                 # groups without their arrays
+    assert call(entry=1, ps=0) == _lib.PA_ERR_ARG                 # cascade plans are split-K
+    assert call(entry=2, mq=8) == _lib.PA_ERR_ARG                 # no query map
+    assert call(entry=2, mq=65, qsl=FAKE) == _lib.PA_ERR_UNSUPPORTED
+    assert call(entry=1, B=4000, ng=200, gs=FAKE) == _lib.PA_ERR_UNSUPPORTED
     assert call(nbytes=64) == _lib.PA_ERR_ARG                     # smaller than the plan
     assert call(hq=7) == _lib.PA_ERR_ARG
     assert call(d=96) == _lib.PA_ERR_UNSUPPORTED

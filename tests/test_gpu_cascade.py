@@ -35,9 +35,9 @@ def _case(q_dtype, cache, hq, hkv, d, seed, lens=LENS, groups=GROUPS):
                           prefix_groups=groups)
 
 
-def _check(w, ps, extra_empty_groups=0):
+def _check(w, ps, extra_empty_groups=0, planned=False):
     pool = gpu_pool(w)
-    out, (pm, psum, po) = run_cascade(w, pool, ps, extra_empty_groups)
+    out, (pm, psum, po) = run_cascade(w, pool, ps, extra_empty_groups, planned=planned)
     torch.cuda.synchronize()
     kp, vp = oracle_pool(w)
     ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
@@ -119,3 +119,30 @@ def test_cascade_full_size_prefix_shared_config():
     ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
                             w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size, seqs=seqs)
     assert max_abs_err(as_f64(out_c)[seqs], ref[seqs]) <= tol
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (16, 1, 64), (12, 4, 128), (4, 4, 64)])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_planned_cascade_matches_oracle(cache, hq, hkv, d):
+    """Through a launch plan (cost-balanced ranges, no per-launch prologue):
+    the oracle's outputs and partials, with empty groups too."""
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = _case(q_dtype, cache, hq, hkv, d, seed=hq * 7 + d + 5)
+    _check(w, 64, planned=True)
+    _check(w, 64, extra_empty_groups=2, planned=True)
+
+
+def test_planned_cascade_full_size_repeats_exactly():
+    """The prefix-shared configuration through a plan: two launches agree bit
+    for bit, and sampled rows match the oracle."""
+    w = make_config(3, device="cuda")
+    pool = gpu_pool(w)
+    out1, _ = run_cascade(w, pool, 256, planned=True)
+    out2, _ = run_cascade(w, pool, 256, planned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    seqs = [0, 1, 7, 8, 100, w.batch - 1]
+    kp, vp = oracle_pool(w, seqs=seqs)
+    ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                            w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size, seqs=seqs)
+    assert max_abs_err(as_f64(out1)[seqs], ref[seqs]) <= TOL[w.cache_dtype]

@@ -33,9 +33,9 @@ def _case(cache, hq, hkv, d, chunks, seed):
                           num_heads=hq, num_kv_heads=hkv, head_dim=d, prefill_chunks=chunks)
 
 
-def _check(w, ps):
+def _check(w, ps, planned=False):
     pool = gpu_pool(w)
-    out, (pm, psum, po), tl = run_multi(w, pool, ps)
+    out, (pm, psum, po), tl = run_multi(w, pool, ps, planned=planned)
     torch.cuda.synchronize()
     kp, vp = oracle_pool(w)
     ref = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
@@ -109,3 +109,24 @@ def test_spec_verify_workload_full_size():
     rows = np.concatenate([np.arange(w.query_start_loc[c], w.query_start_loc[c + 1])
                            for c in chunks])
     assert max_abs_err(as_f64(out)[rows], ref[rows]) <= TOL[w.cache_dtype]
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (8, 8, 64), (12, 4, 128)])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_planned_multi_query_matches_oracle(cache, hq, hkv, d):
+    """Through a launch plan: the prefill oracle's outputs and the decode
+    oracle's per-token partials."""
+    w = _case(cache, hq, hkv, d, CHUNKS, seed=hq + d + 9)
+    _check(w, 64, planned=True)
+
+
+def test_planned_spec_verify_full_size_repeats_exactly():
+    w = make_spec_verify(device="cuda")
+    pool = gpu_pool(w)
+    out1, _, _ = run_multi(w, pool, 256, planned=True)
+    out2, _, _ = run_multi(w, pool, 256, planned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    want, _, _ = run_multi(w, pool, 256)
+    g, r = as_f64(out1), as_f64(want)
+    assert np.max(np.abs(g - r)) <= TOL[w.cache_dtype]
