@@ -139,9 +139,11 @@ def main():
         g_start, g_seqs, g_plens = i32(g_start), i32(g_seqs), i32(g_plens)
         g_max = max(len(m) for m, _ in w.prefix_groups)
     has_prefill = w.num_chunks > 0 and not spec
-    # plain decode steps append each sequence's new token inside the decode launch
-    fused = not (spec or cascade or has_prefill or args.no_fuse_append)
-    if fused:
+    # plain and cascade decode steps append each sequence's new token inside
+    # the decode launch (fused: the plain step's pa_decode_append)
+    fuse_append = not (spec or has_prefill or args.no_fuse_append)
+    fused = fuse_append and not cascade
+    if fuse_append:
         rows = np.zeros(B, np.int64)
         fslots = np.full(B, -1, np.int32)
         j = 0
@@ -166,7 +168,7 @@ def main():
         elif cascade:
             extra = dict(groups=(g_start, g_seqs, g_plens, g_max))
         pa_decode_plan(plan, bt, lens, w.num_heads, pools[0].k, pools[0].v, partition_size=ps,
-                       max_partitions=pmax, **extra)
+                       max_partitions=pmax, new_slots=fslots if fuse_append else None, **extra)
     if has_prefill:
         qp = w.q_prefill.contiguous()
         outp = torch.empty_like(qp)
@@ -183,7 +185,7 @@ def main():
             ev[0].record(stream)
         if planned and layer % PLAN_LAYERS == 0:
             make_plan()
-        if not fused:
+        if not fuse_append:
             pool.append(new_k, new_v, new_slots)
         if ev is not None:
             ev[1].record(stream)
@@ -213,9 +215,10 @@ def main():
             pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
                             part_sum, part_out, pool.k_scale, pool.v_scale, plan=plan)
         elif cascade:
+            appended = dict(k_new=fk, v_new=fv, new_slots=fslots) if fuse_append else {}
             pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, g_start, g_seqs, g_plens, g_max,
                               ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale,
-                              plan=plan)
+                              plan=plan, **appended)
         elif planned:
             pa_decode_append(out if ps == 0 else None, q, None, None, None, pool.k, pool.v, bt,
                              lens, w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
@@ -292,7 +295,8 @@ def main():
         step(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
     names = (["(append fused)" + (", plan / %d layers" % PLAN_LAYERS if planned else ""),
-              "decode_append"] if fused else ["kv_append", "decode"]) + \
+              "decode_append" if fused else "decode"] if fuse_append else
+             ["kv_append", "decode"]) + \
         ["splitk_reduce", "prefill_chunk"]
     names = names[:nev - 1]
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
@@ -344,7 +348,9 @@ def main():
             "pool_blocks": w.num_blocks, "layer_copies": R,
             "decode_entry": result_entry,
             "plan": ("pa_decode_plan once per %d layer-steps" % PLAN_LAYERS) if planned else None,
-            "step_entries": ("pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
+            "step_entries": ("pa_decode_cascade (append fused) + pa_decode_splitk_reduce"
+                             if fuse_append and cascade else
+                             "pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (
                                  result_entry,

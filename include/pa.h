@@ -201,6 +201,10 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
  *               the cascade).  The workgroup count depends on the device's
  *               compute units.
  *   entry       the decode entry point that will use the plan
+ *   new_slots   NULL, or the new_slots the launches will append with (append
+ *               and cascade entries): the plan then lists, per wavefront,
+ *               the tokens it writes (checked against the tables once), so
+ *               the launch loads all their rows at once
  *   group_*, num_groups, max_group_size   the cascade's groups (else NULL, 0)
  *   query_start_loc, max_query_len        pa_decode_multi's query map (else
  *                                         NULL, 0)
@@ -209,14 +213,15 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
  * tiles across workgroups: an item counts one extra tile, for its Q load and
  * its partial write, so many short items weigh like a few long ones.
  * The plan stays valid while context_lens, the first ceil(L_b / 16)
- * block-table entries of every row, and the groups or query map are
- * unchanged.  It follows the stream: the plan launch must precede its users
+ * block-table entries of every row, new_slots, and the groups or query map
+ * are unchanged.  It follows the stream: the plan launch must precede its users
  * on that stream, or be otherwise ordered before them.
  */
 size_t pa_decode_plan_bytes(int32_t rows, pa_dtype_t cache_dtype, int32_t head_dim);
 pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_entry_t entry,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t batch,
+                           const int32_t* new_slots,
                            const int32_t* group_start, const int32_t* group_seqs,
                            const int32_t* group_prefix_lens, int32_t num_groups,
                            int32_t max_group_size, const int32_t* query_start_loc,
@@ -250,10 +255,14 @@ pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_entry_t ent
  * batch + num_groups <= 4096 (PA_ERR_UNSUPPORTED otherwise).  num_groups == 0
  * computes exactly what pa_decode computes.
  */
-/* plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_CASCADE
+/* k_new, v_new, new_slots: NULL, or each sequence's newest token appended
+ * in the same launch, as pa_decode_append does (a token in a prefix-shared
+ * block carries slot -1).
+ * plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_CASCADE
  * (see pa_decode_plan). */
 pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
-                              const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                              const void* k_new, const void* v_new, const int32_t* new_slots,
+                              void* k_cache, void* v_cache, pa_dtype_t cache_dtype,
                               const float* k_scale, const float* v_scale,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t batch,

@@ -50,11 +50,12 @@ def load(path=LIB_PATH):
     lib.pa_decode_append.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                      i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
                                      ctypes.c_size_t, st]
-    lib.pa_decode_plan.argtypes = [vp, ctypes.c_size_t, i32, vp, i32, vp, i32, vp, vp, vp, i32, i32,
-                                   vp, i32, i32, i32, i32, i32, i32, i32, st]
+    lib.pa_decode_plan.argtypes = [vp, ctypes.c_size_t, i32, vp, i32, vp, i32, vp, vp, vp, vp, i32,
+                                   i32, vp, i32, i32, i32, i32, i32, i32, i32, st]
     lib.pa_decode_plan_bytes.argtypes = [i32, i32, i32]
     lib.pa_decode_plan_bytes.restype = ctypes.c_size_t
-    lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp, vp, vp,
+    lib.pa_decode_cascade.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
+                                      vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
                                       ctypes.c_size_t, st]
     lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
@@ -166,12 +167,12 @@ PA_PLAN_DECODE_APPEND, PA_PLAN_DECODE_CASCADE, PA_PLAN_DECODE_MULTI = 0, 1, 2
 
 
 def pa_decode_plan(plan, block_tables, context_lens, num_heads, k_cache, v_cache, partition_size=0,
-                   max_partitions=1, groups=None, queries=None, stream=None):
+                   max_partitions=1, groups=None, queries=None, new_slots=None, stream=None):
     """Fill `plan` (from decode_plan_buffer) with the decode prologue of this
     batch for launches with the same arguments: pa_decode_append by default;
     pa_decode_cascade with groups=(group_start, group_seqs, group_prefix_lens,
     max_group_size); pa_decode_multi with queries=(query_start_loc,
-    max_query_len)."""
+    max_query_len).  new_slots: the slots the launches will append with."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     B = context_lens.numel()
     if block_tables.shape[0] != B:
@@ -189,7 +190,9 @@ def pa_decode_plan(plan, block_tables, context_lens, num_heads, k_cache, v_cache
         qsl = _i32(qsl, "query_start_loc")
     st = load().pa_decode_plan(_plan_ptr(plan), _plan_bytes(plan), entry,
                                _i32(block_tables, "block_tables"), block_tables.shape[1],
-                               _i32(context_lens, "context_lens"), B, gs, gq, gp, ng, int(mg), qsl,
+                               _i32(context_lens, "context_lens"), B,
+                               None if new_slots is None else _i32(new_slots, "new_slots"),
+                               gs, gq, gp, ng, int(mg), qsl,
                                int(mq), int(num_heads), hkv, d, _dt(k_cache), int(partition_size),
                                int(max_partitions), _stream(stream))
     _check("pa_decode_plan", st)
@@ -281,7 +284,7 @@ def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_ta
 def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, group_start,
                       group_seqs, group_prefix_lens, max_group_size, partition_size,
                       max_partitions, part_max, part_sum, part_out, k_scale=None, v_scale=None,
-                      plan=None, stream=None):
+                      plan=None, k_new=None, v_new=None, new_slots=None, stream=None):
     """Split-K partials like pa_decode, reading each prefix group's shared
     partitions once for up to 16/G members at a time.  group_start int32
     [num_groups + 1], group_seqs int32 [members], group_prefix_lens int32
@@ -301,7 +304,14 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, gr
     ng = group_prefix_lens.numel()
     if group_start.numel() != ng + 1:
         raise ValueError("group_start must have num_groups + 1 entries")
-    st = load().pa_decode_cascade(_ptr(q), _dt(q), _ptr(k_cache), _ptr(v_cache), _dt(k_cache),
+    if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots is None):
+        raise ValueError("k_new, v_new and new_slots go together")
+    if k_new is not None and (tuple(k_new.shape) != (B, hkv, d) or k_new.dtype != q.dtype
+                              or tuple(v_new.shape) != (B, hkv, d) or new_slots.numel() != B):
+        raise ValueError("k_new/v_new must be [B, num_kv_heads, head_dim] of q's dtype")
+    st = load().pa_decode_cascade(_ptr(q), _dt(q), _ptr(k_new), _ptr(v_new),
+                                  None if new_slots is None else _i32(new_slots, "new_slots"),
+                                  _ptr(k_cache), _ptr(v_cache), _dt(k_cache),
                                   _ptr(k_scale), _ptr(v_scale), _i32(block_tables, "block_tables"),
                                   block_tables.shape[1], _i32(context_lens, "context_lens"), B,
                                   _i32(group_start, "group_start"), _i32(group_seqs, "group_seqs"),

@@ -52,17 +52,20 @@ constexpr int kMaxMultiQuery = 64;     // query tokens per sequence in pa_decode
 //   [16 + R, 16 + 2R)   the row's aux word (plain rows: tiles per KV head)
 //   [16 + 2R, 17 + 3R)  exclusive prefix of tiles (R + 1 entries)
 // for R rows (the sequences, then any prefix groups).
-//   then, 16-aligned, 16 words per wavefront (grid x 4): first and end tile,
+//   then, 16-aligned, 32 words per wavefront (grid x 4): first and end tile,
 //   its workgroup's first and end tile, the rows of its first and last tile,
-//   the block ids of its first tile (4 words) and of its second (4 words).
+//   the block ids of its first tile (4 words) and of its second (4 words),
+//   the number of new tokens it appends (-1: not listed) and, from word 16,
+//   up to kPlanMaxAppends (row * num_kv_heads + head, slot) pairs.
 enum { kRun = 0, kMakePlan = 1, kUsePlan = 2 };
 constexpr int kPlanMagic = 0x50414450;
 enum {
     kPlanMagicW, kPlanBatch, kPlanKvHeads, kPlanPS, kPlanMaxPart, kPlanTT, kPlanGrid, kPlanNW,
-    kPlanMaxBlocks, kPlanSplit, kPlanTiles, kPlanHeadDim, kPlanRows, kPlanRowKind,
+    kPlanMaxBlocks, kPlanSplit, kPlanTiles, kPlanHeadDim, kPlanRows, kPlanRowKind, kPlanAppends,
     kPlanHeader = 16
 };
-constexpr int kPlanWave = 16;
+constexpr int kPlanWave = 32;
+constexpr int kPlanMaxAppends = 8;     // tokens a wavefront's words can list
 __host__ __device__ constexpr long plan_waves_offset(int batch) {
     return ((long)kPlanHeader + 3L * batch + 1 + 15) / 16 * 16;
 }
@@ -90,8 +93,8 @@ struct DecodeArgs {
     // query_start_loc[b] .. query_start_loc[b+1]-1 of q and of the partials,
     // at positions L_b - q_len_b .. L_b - 1 (causal among themselves)
     const int32_t* query_start_loc;
-    // fused append (plain decode): sequence b's newest token, at position
-    // L_b - 1, goes to slot new_slots[b] (-1: already in the pool)
+    // fused append (plain decode, cascade): sequence b's newest token, at
+    // position L_b - 1, goes to slot new_slots[b] (-1: already in the pool)
     const void* k_new;
     const void* v_new;
     const int32_t* new_slots;
@@ -176,6 +179,8 @@ void decode_kernel(DecodeArgs a) {
     // wavefront's tile ranges, the rows of the wavefront's first and last tile
     int T = 0, wg_a = 0, wg_e = 0, g0 = 0, g1 = 0, rg0 = 0, rg1 = 0;
     int plan_ids[2][Ops::TB];                    // block ids of the first two tiles (from a plan)
+    int plan_apps = -1;                          // tokens this wavefront appends (a plan's list)
+    int plan_app_rh[kPlanMaxAppends], plan_app_slot[kPlanMaxAppends];
     bool plan_ok = true;
     if constexpr (MODE == kUsePlan) {
         // header and this wavefront's words: scalar loads; the row table
@@ -205,6 +210,12 @@ void decode_kernel(DecodeArgs a) {
         for (int j = 0; j < Ops::TB; ++j) {
             plan_ids[0][j] = load_invariant(wv + 6 + j);
             plan_ids[1][j] = load_invariant(wv + 10 + j);
+        }
+        plan_apps = load_invariant(pl + kPlanAppends) == 1 ? load_invariant(wv + 14) : -1;
+#pragma unroll
+        for (int i = 0; i < kPlanMaxAppends; ++i) {
+            plan_app_rh[i] = load_invariant(wv + 16 + 2 * i);
+            plan_app_slot[i] = load_invariant(wv + 17 + 2 * i);
         }
         for (int r = tid; r < R; r += NT) {
             s_len[r] = pl[kPlanHeader + r];
@@ -485,9 +496,11 @@ void decode_kernel(DecodeArgs a) {
     // b's new token for head h there before loading anything.  A wavefront's
     // vector memory accesses to one address are performed in order, so its
     // later K/V loads of that block return the new token without a wait.
-    if (PLAIN && MODE != kMakePlan && a.new_slots != nullptr && ntiles > 0) {
-        constexpr int IB = KIND == kF32 ? 4 : 2;          // input element bytes
-        for (int r = rg0; r <= rg1; ++r) {
+    // (sequence rows only: plain decode and the cascade's member rows)
+    constexpr int IB = KIND == kF32 ? 4 : 2;              // input element bytes
+    // f(r, h, slot) for each token this wavefront writes, in order
+    auto for_each_append = [&](auto&& f) {
+        for (int r = rg0; r <= min(rg1, B - 1); ++r) {
             const int th = row_head_tiles(r);
             if (th == 0) continue;
             const int base = s_tpre[r];
@@ -503,15 +516,48 @@ void decode_kernel(DecodeArgs a) {
             if (slot < 0 || slot != want) continue;
             for (int h = h0; h < Hkv; ++h) {
                 if (base + (h + 1) * th - 1 >= g1) break;
+                f(r, h, slot);
+            }
+        }
+    };
+    auto scales = [&](int h, float& ksc, float& vsc) {
+        ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
+        vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
+    };
+    if (MODE != kMakePlan && a.new_slots != nullptr && ntiles > 0) {
+        if (MODE == kUsePlan && plan_apps >= 0) {
+            // the plan's list: every row's loads go out before the first store
+            if (plan_apps > 0) {
+                TokenChunk<KIND> tok[kPlanMaxAppends];
+#pragma unroll
+                for (int i = 0; i < kPlanMaxAppends; ++i) {
+                    const long row = (long)plan_app_rh[min(i, plan_apps - 1)] * D * IB;
+                    tok[i] = load_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
+                                                       static_cast<const char*>(a.v_new) + row,
+                                                       lane & (D / 8 - 1));
+                }
+#pragma unroll
+                for (int i = 0; i < kPlanMaxAppends; ++i) {
+                    if (i >= plan_apps) break;
+                    const int h = plan_app_rh[i] % Hkv, slot = plan_app_slot[i];
+                    float ksc, vsc;
+                    scales(h, ksc, vsc);
+                    if (lane < D / 8)
+                        store_token_chunk<KIND, D>(tok[i], a.k_cache_w, a.v_cache_w, slot / kBlock,
+                                                   slot % kBlock, h, Hkv, lane, ksc, vsc);
+                }
+            }
+        } else {
+            for_each_append([&](int r, int h, int slot) {
                 const long row = ((long)r * Hkv + h) * D * IB;
-                const float ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
-                const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
+                float ksc, vsc;
+                scales(h, ksc, vsc);
                 if (lane < D / 8)
                     write_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
                                                static_cast<const char*>(a.v_new) + row,
                                                a.k_cache_w, a.v_cache_w, slot / kBlock,
                                                slot % kBlock, h, Hkv, lane, ksc, vsc);
-            }
+            });
         }
     }
 
@@ -602,6 +648,17 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < 6; ++k)
             if (lane == k) w = vals[k];
+        // the tokens this wavefront appends, checked against the tables now
+        int napp = 0;
+        if (a.new_slots != nullptr && ntiles > 0)
+            for_each_append([&](int r, int h, int slot) {
+                if (napp < kPlanMaxAppends) {
+                    if (lane == 16 + 2 * napp) w = r * Hkv + h;
+                    if (lane == 17 + 2 * napp) w = slot;
+                }
+                ++napp;
+            });
+        if (lane == 14) w = a.new_slots == nullptr || napp > kPlanMaxAppends ? -1 : napp;
         if (lane < kPlanWave) wv[lane] = w;
         if (blockIdx.x == 0) {
             for (int r = tid; r < R; r += NT) {
@@ -612,7 +669,7 @@ void decode_kernel(DecodeArgs a) {
             if (tid < kPlanHeader) {
                 const int hdr[kPlanHeader] = {kPlanMagic, B, Hkv, PS, a.max_partitions, TT,
                                               (int)gridDim.x, NW, a.max_blocks_per_seq, a.split,
-                                              T, D, R, row_kind, 0, 0};
+                                              T, D, R, row_kind, a.new_slots != nullptr, 0};
                 int v = 0;
 #pragma unroll
                 for (int k = 0; k < kPlanHeader; ++k)
@@ -1033,6 +1090,21 @@ static pa_status_t set_multi(DecodeArgs& a, const int32_t* query_start_loc, int 
     return PA_OK;
 }
 
+// The fused append's arrays: all three, or none.
+static pa_status_t set_append(DecodeArgs& a, const void* k_new, const void* v_new,
+                              const int32_t* new_slots, void* k_cache, void* v_cache) {
+    const int given = (k_new != nullptr) + (v_new != nullptr) + (new_slots != nullptr);
+    if (given != 0 && given != 3) return PA_ERR_ARG;
+    if (given == 3) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.new_slots = new_slots;
+        a.k_cache_w = static_cast<char*>(k_cache);
+        a.v_cache_w = static_cast<char*>(v_cache);
+    }
+    return PA_OK;
+}
+
 // A plan buffer for `rows` rows large enough for every word a launch reads.
 static bool plan_fits(size_t plan_bytes, int rows, pa_dtype_t cache_dtype, int head_dim);
 
@@ -1076,15 +1148,8 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
                                  num_heads, num_kv_heads, head_dim, block_size, scale,
                                  partition_size, max_partitions, part_max, part_sum, part_out);
     if (st != PA_OK || batch == 0) return st;
-    const int given = (k_new != nullptr) + (v_new != nullptr) + (new_slots != nullptr);
-    if (given != 0 && given != 3) return PA_ERR_ARG;
-    if (given == 3) {
-        a.k_new = k_new;
-        a.v_new = v_new;
-        a.new_slots = new_slots;
-        a.k_cache_w = static_cast<char*>(k_cache);
-        a.v_cache_w = static_cast<char*>(v_cache);
-    }
+    st = set_append(a, k_new, v_new, new_slots, k_cache, v_cache);
+    if (st != PA_OK) return st;
     if (plan) {
         // every word the launch may read lies inside the buffer
         if (!plan_fits(plan_bytes, batch, cache_dtype, head_dim)) return PA_ERR_ARG;
@@ -1095,7 +1160,8 @@ extern "C" pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_d
 }
 
 extern "C" pa_status_t pa_decode_cascade(
-    const void* q, pa_dtype_t q_dtype, const void* k_cache, const void* v_cache,
+    const void* q, pa_dtype_t q_dtype, const void* k_new, const void* v_new,
+    const int32_t* new_slots, void* k_cache, void* v_cache,
     pa_dtype_t cache_dtype, const float* k_scale, const float* v_scale,
     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
     int32_t batch, const int32_t* group_start, const int32_t* group_seqs,
@@ -1116,6 +1182,8 @@ extern "C" pa_status_t pa_decode_cascade(
     if (batch == 0) return PA_OK;
     long items = 0;
     st = set_cascade(a, group_start, group_seqs, group_prefix_lens, num_groups, max_group_size, items);
+    if (st != PA_OK) return st;
+    st = set_append(a, k_new, v_new, new_slots, k_cache, v_cache);
     if (st != PA_OK) return st;
     if (plan) {
         if (!plan_fits(plan_bytes, batch + num_groups, cache_dtype, head_dim)) return PA_ERR_ARG;
@@ -1170,6 +1238,7 @@ static bool plan_fits(size_t plan_bytes, int rows, pa_dtype_t cache_dtype, int h
 extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_entry_t entry,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* context_lens, int32_t batch,
+                                      const int32_t* new_slots,
                                       const int32_t* group_start, const int32_t* group_seqs,
                                       const int32_t* group_prefix_lens, int32_t num_groups,
                                       int32_t max_group_size, const int32_t* query_start_loc,
@@ -1215,6 +1284,7 @@ extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_
     }
     if (st != PA_OK) return st;
     if (!plan_fits(plan_bytes, rows, cache_dtype, head_dim)) return PA_ERR_ARG;
+    if (entry != PA_PLAN_DECODE_MULTI) a.new_slots = new_slots;
     a.plan_out = plan;
     return run_decode(a, cache_dtype, head_dim, items, entry != PA_PLAN_DECODE_APPEND, stream);
 }

@@ -91,9 +91,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(void* __restrict__ out,
 // Few partitions (max_partitions <= 64): one wavefront per (sequence, query
 // head), four per workgroup.  Lane p holds partition p's (m, l); the weights
 // are broadcast with v_readlane while each lane accumulates D/64 columns.
-// The first U partition rows are loaded together with (m, l), so up to U
-// partitions cost one memory round trip.
-template <int D, bool OUT_BF16>
+// The first U partition rows (U: max_partitions rounded up to a power of two,
+// at most 16) are loaded together with (m, l), so up to U partitions cost one
+// memory round trip.
+template <int D, bool OUT_BF16, int U>
 __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out,
                                                           const float* __restrict__ part_max,
                                                           const float* __restrict__ part_sum,
@@ -102,7 +103,6 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out
                                                           int num_heads, int partition_size,
                                                           int max_partitions, int npairs) {
     constexpr int C = D / kWave;                       // columns per lane
-    constexpr int U = 16;                              // partition rows in flight
     const int lane = lane_id();
     const int bh = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
     if (bh >= npairs) return;
@@ -167,9 +167,15 @@ static hipError_t launch_reduce(void* out, const float* pm, const float* ps, con
     const long pairs = (long)batch * num_heads;
     if (pairs > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (max_partitions <= kWave) {
-        hipLaunchKernelGGL((reduce_wave_kernel<D, OUT_BF16>), dim3((unsigned)((pairs + 3) / 4)),
-                           dim3(256), 0, stream, out, pm, ps, po, lens, num_heads, partition_size,
-                           max_partitions, (int)pairs);
+        const dim3 grid((unsigned)((pairs + 3) / 4));
+#define PA_REDUCE_WAVE(UU)                                                                    \
+    hipLaunchKernelGGL((reduce_wave_kernel<D, OUT_BF16, UU>), grid, dim3(256), 0, stream, out, \
+                       pm, ps, po, lens, num_heads, partition_size, max_partitions, (int)pairs)
+        if (max_partitions <= 2) PA_REDUCE_WAVE(2);
+        else if (max_partitions <= 4) PA_REDUCE_WAVE(4);
+        else if (max_partitions <= 8) PA_REDUCE_WAVE(8);
+        else PA_REDUCE_WAVE(16);
+#undef PA_REDUCE_WAVE
     } else {
         hipLaunchKernelGGL((reduce_kernel<D, OUT_BF16>), dim3((unsigned)pairs), dim3(256), 0,
                            stream, out, pm, ps, po, lens, num_heads, partition_size,

@@ -147,9 +147,11 @@ def group_arrays(w, extra_empty_groups=0, device="cuda"):
     return i32(start, device), i32(seqs, device), i32(plens, device), mg
 
 
-def run_cascade(w, pool, partition_size, extra_empty_groups=0, device="cuda", planned=False):
+def run_cascade(w, pool, partition_size, extra_empty_groups=0, device="cuda", planned=False,
+                appended=None):
     """pa_decode_cascade + pa_decode_splitk_reduce (optionally through a
-    launch plan); returns (out, (pm, ps, po))."""
+    launch plan, optionally appending (k_new, v_new, new_slots) in the same
+    launch); returns (out, (pm, ps, po))."""
     q = w.q.to(device).contiguous()
     bt, lens = i32(w.block_tables, device), i32(w.context_lens, device)
     pmax = max(1, -(-int(np.max(w.context_lens)) // partition_size))
@@ -162,9 +164,11 @@ def run_cascade(w, pool, partition_size, extra_empty_groups=0, device="cuda", pl
     if planned:
         plan = decode_plan_buffer(B + gs.numel() - 1, pool.k, d, device)
         pa_decode_plan(plan, bt, lens, w.num_heads, pool.k, pool.v, partition_size, pmax,
-                       groups=(gs, gq, gp, mg))
+                       groups=(gs, gq, gp, mg),
+                       new_slots=appended[2] if appended else None)
+    kw = dict(zip(("k_new", "v_new", "new_slots"), appended)) if appended else {}
     pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, gs, gq, gp, mg, partition_size, pmax,
-                      pm, ps, po, pool.k_scale, pool.v_scale, plan=plan)
+                      pm, ps, po, pool.k_scale, pool.v_scale, plan=plan, **kw)
     out = torch.empty_like(q)
     pa_decode_splitk_reduce(out, pm, ps, po, lens, partition_size)
     return out, (pm, ps, po)

@@ -104,7 +104,8 @@ def test_cascade_validation():
 
     def call(ps=256, pmax=4, B=4, ng=1, mgs=4, gs=FAKE, gq=FAKE, gp=FAKE, parts=FAKE, plan=None,
              nbytes=0):
-        return lib.pa_decode_cascade(FAKE, 1, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B, gs,
+        return lib.pa_decode_cascade(FAKE, 1, None, None, None, FAKE, FAKE, 1, None, None, FAKE, 32,
+                                     FAKE, B, gs,
                                      gq, gp, ng, mgs, 8, 2, 128, 16, 0.1, ps, pmax, parts, parts,
                                      parts, plan, nbytes, None)
 
@@ -156,8 +157,8 @@ def test_decode_plan_validation():
 
     def call(plan=FAKE, nbytes=1 << 20, entry=0, B=4, hq=8, hkv=2, d=128, c_dt=1, ps=64, pmax=4,
              gs=None, ng=0, qsl=None, mq=0):
-        return lib.pa_decode_plan(plan, nbytes, entry, FAKE, 32, FAKE, B, gs, gs, gs, ng, 4, qsl,
-                                  mq, hq, hkv, d, c_dt, ps, pmax, None)
+        return lib.pa_decode_plan(plan, nbytes, entry, FAKE, 32, FAKE, B, None, gs, gs, gs, ng, 4,
+                                  qsl, mq, hq, hkv, d, c_dt, ps, pmax, None)
 
     assert call(plan=None) == _lib.PA_ERR_ARG
     assert call(entry=3) == _lib.PA_ERR_ARG

@@ -146,3 +146,28 @@ def test_planned_cascade_full_size_repeats_exactly():
     ref = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
                             w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size, seqs=seqs)
     assert max_abs_err(as_f64(out1)[seqs], ref[seqs]) <= TOL[w.cache_dtype]
+
+
+@pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_cascade_fused_append_equals_append_then_cascade(cache, planned):
+    """Each member's newest token appended by the cascade launch itself (slot
+    -1 for tokens in shared blocks): the pools and outputs of pa_kv_append
+    followed by pa_decode_cascade, bit for bit."""
+    from paged_kv_cache_234_amd import pa_kv_append
+    from tests.gpu_helpers import decode_new_tokens
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = _case(q_dtype, cache, 8, 2, 128, seed=61)
+    k_new, v_new, slots = decode_new_tokens(w)
+    assert int((slots < 0).sum()) >= 2
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    pa_kv_append(k_new, v_new, pool_a.k, pool_a.v, slots, pool_a.k_scale, pool_a.v_scale)
+    want, parts_a = run_cascade(w, pool_a, 64, planned=planned)
+    got, parts_b = run_cascade(w, pool_b, 64, planned=planned,
+                               appended=(k_new, v_new, slots))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
+    assert torch.equal(got, want)
+    for a, b in zip(parts_a, parts_b):
+        assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))

@@ -135,12 +135,15 @@ def test_fused_append_ignores_a_slot_off_the_table():
     assert torch.equal(pool.v.view(torch.uint8), before_v.view(torch.uint8))
 
 
-def _plan_for(w, pool, ps):
+def _plan_for(w, pool, ps, listed=True):
+    """A plan for pa_decode_append over w; listed: it also lists each
+    wavefront's appended tokens (made with the launch's new_slots)."""
     from paged_kv_cache_234_amd import decode_plan_buffer, pa_decode_plan
     pmax = max(1, -(-int(np.max(w.context_lens)) // ps)) if ps else 1
     plan = decode_plan_buffer(w.batch, pool.k, w.head_dim)
     pa_decode_plan(plan, i32(w.block_tables), i32(w.context_lens), w.num_heads, pool.k, pool.v,
-                   partition_size=ps, max_partitions=pmax)
+                   partition_size=ps, max_partitions=pmax,
+                   new_slots=decode_new_tokens(w)[2] if listed else None)
     return plan
 
 
@@ -164,10 +167,11 @@ def _run_planned(w, pool, ps, plan, out_fill=float("nan")):
     return out, (pm, psum, po)
 
 
+@pytest.mark.parametrize("listed", [True, False])
 @pytest.mark.parametrize("ps", [0, 64, 256])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
-def test_planned_launch_equals_unplanned(cache, d, ps):
+def test_planned_launch_equals_unplanned(cache, d, ps, listed):
     """A launch that reads its prologue from a plan gives the pools, outputs
     and partials of the launch that computes it, bit for bit."""
     q_dtype = "f32" if cache == "f32" else "bf16"
@@ -176,7 +180,7 @@ def test_planned_launch_equals_unplanned(cache, d, ps):
                        decode_lens=LENS)
     pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
     want, parts_a = _run(w, pool_a, ps, fused=True)
-    plan = _plan_for(w, pool_b, ps)
+    plan = _plan_for(w, pool_b, ps, listed)
     got, parts_b = _run_planned(w, pool_b, ps, plan)
     assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
     assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
@@ -221,4 +225,18 @@ def test_planned_launch_full_size(cfg, ps):
     want, _ = _run(w, pool_a, ps, fused=True)
     got, _ = _run_planned(w, pool_b, ps, _plan_for(w, pool_b, ps))
     assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(got, want)
+
+
+def test_planned_append_list_overflow_falls_back_to_the_scan():
+    """Waves holding more new tokens than a plan lists (4096 one-tile
+    sequences over 4 KV heads: 16 per wave) scan for them as unplanned
+    launches do: the same pools and outputs."""
+    w = build_workload("fov", seed=41, device="cuda", num_heads=8, num_kv_heads=4, head_dim=64,
+                       decode_lens=[16] * 4096)
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    want, _ = _run(w, pool_a, 64, fused=True)
+    got, _ = _run_planned(w, pool_b, 64, _plan_for(w, pool_b, 64))
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
     assert torch.equal(got, want)
