@@ -90,6 +90,20 @@ __device__ __forceinline__ float max_over_groups(float x) {
     permlane16_swap(c, d);
     return fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
 }
+// The same maximum, NaN-propagating (v_maximum3): unlike fmaxf it needs no
+// canonicalisation of the exchanged values.
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float max_over_groups_nan(float x) {
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    permlane32_swap(a, b);
+    uint32_t c = __builtin_bit_cast(uint32_t,
+                                    fmax_nan(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+    uint32_t d = c;
+    permlane16_swap(c, d);
+    return fmax_nan(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
+}
 __device__ __forceinline__ float sum_over_groups(float x) {
     uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
     permlane32_swap(a, b);

@@ -14,6 +14,8 @@
 // wavefront walks key tiles 0 .. (its last position) with the next tile's
 // loads in flight, masking per column only on the tiles that cross a causal
 // boundary or the end of the context.
+#include <cfloat>
+
 #include "pa_internal.hpp"
 #include "pa_tiles.hpp"
 
@@ -35,6 +37,8 @@ struct PrefillArgs {
     int group;          // G
     int npos;           // query positions per 16-column tile
     int wg_per_head;    // workgroups per (chunk, KV head)
+    int num_chunks;
+    int num_cus;        // compute units: the stride between workgroups sharing one
     float scale_log2;
 };
 
@@ -144,7 +148,7 @@ void prefill_kernel(PrefillArgs a) {
 // id is wave-uniform, a scalar load), widens fp8 to bf16 on the way, and
 // writes it in the layouts the bf16 MFMA operands read as one contiguous
 // 1 KB per wave-wide 16-byte LDS read:
-//   K  [block][D/8][16 tokens][8 dims]            (the bf16 pool layout)
+//   K  [half][M-tile][D/8][16 rows][8 dims]       (rows in key-pair order)
 //   V  [half][D/16][key run q][16 dims][8 keys]   (half = 32 positions; run q
 //                                                  = keys 8q .. 8q+7)
 // Each wavefront then runs NC 16-column query tiles over the tile, two
@@ -155,10 +159,122 @@ void prefill_kernel(PrefillArgs a) {
 constexpr int kLdsTile = 64;                  // positions per staged tile (4 blocks)
 constexpr int kLdsCols = 2;                   // 16-column query tiles per wavefront
 
+// Staged K rows in key-pair order: in each 32-position half, M-tile i row
+// 4j + e holds key 8j + 4i + e.  After QK^T lane group j then holds keys
+// 8j .. 8j+7 of its query column (M-tile 0: 8j .. 8j+3, M-tile 1: 8j+4 ..
+// 8j+7), which is already the PV operand layout: no lane exchange.
+template <int D> struct StagedOps : TileOps<kBF16, D> {
+    using Base = TileOps<kBF16, D>;
+    using Regs = typename Base::Regs;
+    static constexpr int NMT = Base::NMT, NVT = Base::NVT;
+    __device__ static int pos(int i, int e, int grp) { return 8 * grp + 4 * i + e; }
+    // M-tile and row of key k (< 32) of a half
+    __host__ __device__ static constexpr int tile_of(int k) { return (k >> 2) & 1; }
+    __host__ __device__ static constexpr int row_of(int k) { return 4 * (k >> 3) + (k & 3); }
+    // S^T of query tile n is complete before tile n + 1's is started
+    template <int NC>
+    __device__ static void qk(const Regs& r, const typename Base::Q (&q)[NC],
+                              f32x4 (&s)[NC][NMT]) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+            for (int i = 0; i < NMT; ++i) {
+                s[n][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < Base::NS; ++k)
+                    s[n][i] = mfma_bf16(as_bf16x8(r.k[i][k]), q[n].op[k], s[n][i]);
+            }
+    }
+    // O^T of one query tile from its probabilities
+    __device__ static void pv_column(const Regs& r, const float (&p)[NMT][4], f32x4 (&o)[NVT]) {
+        const bf16x8 b = as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                                         pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) o[t] = mfma_bf16(as_bf16x8(r.v[t]), b, o[t]);
+    }
+};
+
+// Launch order.  Workgroups are placed breadth-first over the CUs, so block b
+// shares its CU with blocks b +- num_cus, and a CU's time is set by the sum of
+// its workgroups' tiles.  Items (chunk, KV head, row group) are ranked by tile
+// count, longest first (ties: KV head, chunk, row group), and pass p of
+// num_cus blocks takes ranks p * num_cus .. in alternating direction: the
+// longest items share a CU with the shortest (longest-processing-time order).
+// Every (chunk, row group) class's count is held in registers, 64 per
+// register: up to 64 * kOrderGroups classes, else the natural order.
+constexpr int kOrderGroups = 8;
+
+__device__ __forceinline__ int launch_rank(int b, int nblocks, int stride) {
+    const int p = b / stride, pos = b - p * stride;
+    const int m = min(stride, nblocks - p * stride);           // blocks in pass p
+    return p * stride + ((p & 1) ? m - 1 - pos : pos);
+}
+
+// (chunk c, KV head h, row group tg) of the item at rank r; false: no work
+__device__ bool item_at_rank(const PrefillArgs& a, int rows, int r, int lane, int& c, int& h,
+                             int& tg) {
+    const int wpg = a.wg_per_head, ncls = a.num_chunks * wpg;
+    int cost[kOrderGroups];                    // tiles of class 64 g + lane (0: no rows)
+#pragma unroll
+    for (int g = 0; g < kOrderGroups; ++g) {
+        const int cls = 64 * g + lane;
+        cost[g] = 0;
+        if (cls < ncls) {
+            const int cc = cls / wpg, t = cls - cc * wpg;
+            const int q0 = a.query_start_loc[cc];
+            const int C = a.query_start_loc[cc + 1] - q0;
+            const int P = a.context_lens[cc] - C;
+            if (P >= 0 && t * rows < C) {
+                const int kend = P + min(C, rows * (t + 1));
+                cost[g] = (kend - 1) / kLdsTile + 1;
+            }
+        }
+    }
+    const int ngroups = (ncls + 63) / 64;
+    auto count_ge = [&](int x) {             // classes with at least x tiles
+        int n = 0;
+#pragma unroll
+        for (int g = 0; g < kOrderGroups; ++g)
+            if (g < ngroups) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(cost[g] >= x));
+        return n;
+    };
+    const int H = a.num_kv_heads;
+    // the item's tile count: the largest x with H * count_ge(x) > r
+    int x = 0;
+    for (int bit = 25; bit >= 0; --bit) {
+        const int cand = x | (1 << bit);
+        if ((long)H * count_ge(cand) > r) x = cand;
+    }
+    if (x == 0) return false;
+    const int above = count_ge(x + 1), ncl = count_ge(x) - above;
+    const int j = r - H * above;               // among the H * ncl items with x tiles
+    h = j / ncl;
+    int k = j - h * ncl;                       // the k-th class with x tiles, by index
+    int cls = 0;
+#pragma unroll
+    for (int g = 0; g < kOrderGroups; ++g) {
+        if (g >= ngroups) break;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cost[g] == x);
+        const int n = __builtin_popcountll(m);
+        if (k < n) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(cost[g] == x && below == k);
+            cls = 64 * g + __builtin_ctzll(hit);
+            break;
+        }
+        k -= n;
+    }
+    c = cls / wpg;
+    tg = cls - c * wpg;
+    return true;
+}
+
 template <int KIND, int D, int NC>
 __global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_lds_kernel(PrefillArgs a) {
     using Ops = TileOps<kBF16, D>;            // staged operands are bf16 for both caches
+    using SOps = StagedOps<D>;
     using QT = uint16_t;
     constexpr int NW = 4, NS = Ops::NS, NVT = Ops::NVT;
     constexpr int KB = kBlock * D * 2;        // one block's K (or V) in bf16
@@ -169,17 +285,28 @@ void prefill_lds_kernel(PrefillArgs a) {
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int tg = item % a.wg_per_head;
-    const int h = (item / a.wg_per_head) % a.num_kv_heads;
-    const int c = item / (a.wg_per_head * a.num_kv_heads);
+    const int wg_rows = NW * NC * a.npos;
+    int c, h, tg;
+    if (a.num_cus > 0 && a.num_chunks * a.wg_per_head <= 64 * kOrderGroups) {
+        // every wavefront finds the same item (wave-uniform ballots)
+        if (!item_at_rank(a, wg_rows, launch_rank(blockIdx.x, gridDim.x, a.num_cus), lane, c, h,
+                          tg))
+            return;                                       // the whole workgroup
+        c = __builtin_amdgcn_readfirstlane(c);
+        h = __builtin_amdgcn_readfirstlane(h);
+        tg = __builtin_amdgcn_readfirstlane(tg);
+    } else {
+        const int item = xcd_remap(blockIdx.x, gridDim.x);
+        tg = item % a.wg_per_head;
+        h = (item / a.wg_per_head) % a.num_kv_heads;
+        c = item / (a.wg_per_head * a.num_kv_heads);
+    }
 
     const int q0 = a.query_start_loc[c];
     const int C = a.query_start_loc[c + 1] - q0;
     const int L = a.context_lens[c];
     const int P = L - C;
     const int npos = a.npos;
-    const int wg_rows = NW * NC * npos;
     const int wg_row0 = tg * wg_rows;
     if (wg_row0 >= C || P < 0) return;                   // the whole workgroup leaves together
     const int kend = P + min(C, wg_row0 + wg_rows);      // keys [0, kend) are touched
@@ -207,6 +334,18 @@ void prefill_lds_kernel(PrefillArgs a) {
     const int min_last = P + row0;
     float cs = a.scale_log2;
     if (KIND == kFP8) cs *= load_invariant(a.k_scale + h);
+    // the folded softmax takes a positive multiplier: a negative one moves
+    // its sign into Q; zero becomes the least normal float, with which every
+    // exp2 argument rounds as with zero (scores far below 2^100)
+    if (cs < 0.f) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                qop[n].op[k] = as_bf16x8(__builtin_bit_cast(u32x4, qop[n].op[k]) ^ 0x80008000u);
+        cs = -cs;
+    }
+    cs = fmaxf(cs, FLT_MIN);
 
     const int32_t* bt = a.block_tables + (long)c * a.max_blocks_per_seq;
     const long head_stride = (long)kBlock * D * ELEM;
@@ -227,8 +366,13 @@ void prefill_lds_kernel(PrefillArgs a) {
             sv[u] = load16(vb + 16 * (lane + kWave * u));
         }
     };
+    // token tok of the staged block: key 16 (wave & 1) + tok of half wave >> 1
+    auto k_dst = [&](int buf, int chunk, int tok) {
+        const int k = 16 * (wave & 1) + tok;
+        return s_k[buf] + (wave >> 1) * (2 * KB) + SOps::tile_of(k) * KB +
+               (chunk * 16 + SOps::row_of(k)) * 16;
+    };
     auto stage_store = [&](int buf) {
-        char* kd = s_k[buf] + wave * KB;
         char* vd = s_v[buf] + (wave >> 1) * (2 * KB);
         const int run0 = (wave & 1) * 2;
 #pragma unroll
@@ -239,8 +383,8 @@ void prefill_lds_kernel(PrefillArgs a) {
                 const int c16 = piece >> 4, tok = piece & 15;
                 const bf16x8 lo = fp8x8_to_bf16x8(sk[u][0], sk[u][1]);
                 const bf16x8 hi = fp8x8_to_bf16x8(sk[u][2], sk[u][3]);
-                *reinterpret_cast<bf16x8*>(kd + ((2 * c16) * 16 + tok) * 16) = lo;
-                *reinterpret_cast<bf16x8*>(kd + ((2 * c16 + 1) * 16 + tok) * 16) = hi;
+                *reinterpret_cast<bf16x8*>(k_dst(buf, 2 * c16, tok)) = lo;
+                *reinterpret_cast<bf16x8*>(k_dst(buf, 2 * c16 + 1, tok)) = hi;
                 // V piece = dim d, 16 tokens: runs run0 (tokens 0-7) and run0 + 1 (8-15)
                 const int d = piece;
                 const bf16x8 v0 = fp8x8_to_bf16x8(sv[u][0], sv[u][1]);
@@ -249,8 +393,8 @@ void prefill_lds_kernel(PrefillArgs a) {
                 *reinterpret_cast<bf16x8*>(vd + ((t16 * 4 + run0) * 16 + dd) * 16) = v0;
                 *reinterpret_cast<bf16x8*>(vd + ((t16 * 4 + run0 + 1) * 16 + dd) * 16) = v1;
             } else {
-                // K: same layout as the pool; V piece = half of dim d's 32 bytes
-                *reinterpret_cast<u32x4*>(kd + 16 * piece) = sk[u];
+                // K piece = (8-dim chunk, token); V piece = half of dim d's 32 bytes
+                *reinterpret_cast<u32x4*>(k_dst(buf, piece >> 4, piece & 15)) = sk[u];
                 const int d = piece >> 1, half = piece & 1;
                 const int t16 = d >> 4, dd = d & 15;
                 *reinterpret_cast<u32x4*>(vd + ((t16 * 4 + run0 + half) * 16 + dd) * 16) = sv[u];
@@ -258,7 +402,7 @@ void prefill_lds_kernel(PrefillArgs a) {
         }
     };
 
-    WaveSoftmax<kBF16, D, NC> st;
+    WaveSoftmax<kBF16, D, NC, SOps, true> st;
     st.init();
     auto compute = [&](int buf, int t) {
 #pragma unroll
@@ -318,6 +462,11 @@ static hipError_t launch_prefill_lds(PrefillArgs a, int num_chunks, int max_quer
                                      hipStream_t stream) {
     const int rows = 4 * NC * a.npos;
     a.wg_per_head = (max_query_len + rows - 1) / rows;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    a.num_cus = cus;                          // 0: the natural order
     const long grid = (long)num_chunks * a.num_kv_heads * a.wg_per_head;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
@@ -378,6 +527,8 @@ extern "C" pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_d
     a.group = num_heads / num_kv_heads;
     a.npos = 16 / a.group;
     a.wg_per_head = 1;
+    a.num_chunks = num_chunks;
+    a.num_cus = 0;
     a.scale_log2 = scale * kLog2e;
     hipError_t e;
     const int kind = cache_kind(cache_dtype);

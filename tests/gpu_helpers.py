@@ -111,7 +111,7 @@ def run_decode(w, pool, partition_size=0, q=None, block_tables=None, context_len
 
 def run_prefill(w, pool, device="cuda"):
     qp = w.q_prefill.to(device).contiguous()
-    out = torch.empty_like(qp)
+    out = torch.full_like(qp, float("nan"))       # a row the launch skips stays NaN
     qsl = w.query_start_loc
     maxq = int(np.max(np.diff(qsl))) if len(qsl) > 1 else 0
     pa_prefill_chunk(out, qp, i32(qsl, device), maxq, pool.k, pool.v,

@@ -86,3 +86,43 @@ def test_mixed_chunked_prefill_config_sampled_rows():
         ref = opa.attend_rows(qf[a + rows], P + rows, K, V, w.scale)
         assert max_abs_err(got[a + rows], ref) <= TOL["fp8"]
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_prefill_negative_and_zero_scale(cache, scale):
+    """softmax(scale * QK^T) for a negative scale (the kernel moves its sign
+    into Q) and for zero (uniform weights over the visible keys)."""
+    w = _case(cache, 8, 2, 128, [(40, 96), (0, 33)], seed=13)
+    pool = gpu_pool(w)
+    qp = w.q_prefill.cuda().contiguous()
+    out = torch.empty_like(qp)
+    qsl = w.query_start_loc
+    pa_prefill_chunk(out, qp, i32(qsl), int(np.max(np.diff(qsl))), pool.k, pool.v,
+                     i32(w.chunk_block_tables), i32(w.chunk_context_lens), scale, pool.k_scale,
+                     pool.v_scale)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    want = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
+                              w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens, scale,
+                              w.k_scale, w.v_scale, w.block_size)
+    assert max_abs_err(as_f64(out), want) <= TOL[cache]
+
+
+@pytest.mark.parametrize("nchunks", [24, 40])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_prefill_launch_order_many_chunks(cache, nchunks):
+    """Many chunks of mixed lengths (32 rows per workgroup): 24 x 7 (chunk,
+    row group) classes are ranked by tile count across three registers of
+    classes; 40 x 13 classes go past the ranking's limit and take the natural
+    order.  Every row must be written once and match the oracle."""
+    rng = np.random.default_rng(nchunks)
+    rows = 200 if nchunks == 24 else 416
+    chunks = [(int(rng.integers(0, 400)), int(rng.integers(1, rows + 1))) for _ in range(nchunks)]
+    chunks[0] = (int(chunks[0][0]), rows)
+    w = _case(cache, 8, 2, 128, chunks, seed=nchunks + 1)
+    out = run_prefill(w, gpu_pool(w))
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    err = max_abs_err(as_f64(out), _oracle(w, kp, vp))
+    assert err <= TOL[cache], err
