@@ -524,30 +524,10 @@ void decode_kernel(DecodeArgs a) {
         ksc = KIND == kFP8 ? load_invariant(a.k_scale + h) : 1.0f;
         vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
     };
+    // (a plan's list of tokens is written where the first tile is loaded)
+    const bool listed_appends = MODE == kUsePlan && a.new_slots != nullptr && plan_apps >= 0;
     if (MODE != kMakePlan && a.new_slots != nullptr && ntiles > 0) {
-        if (MODE == kUsePlan && plan_apps >= 0) {
-            // the plan's list: every row's loads go out before the first store
-            if (plan_apps > 0) {
-                TokenChunk<KIND> tok[kPlanMaxAppends];
-#pragma unroll
-                for (int i = 0; i < kPlanMaxAppends; ++i) {
-                    const long row = (long)plan_app_rh[min(i, plan_apps - 1)] * D * IB;
-                    tok[i] = load_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
-                                                       static_cast<const char*>(a.v_new) + row,
-                                                       lane & (D / 8 - 1));
-                }
-#pragma unroll
-                for (int i = 0; i < kPlanMaxAppends; ++i) {
-                    if (i >= plan_apps) break;
-                    const int h = plan_app_rh[i] % Hkv, slot = plan_app_slot[i];
-                    float ksc, vsc;
-                    scales(h, ksc, vsc);
-                    if (lane < D / 8)
-                        store_token_chunk<KIND, D>(tok[i], a.k_cache_w, a.v_cache_w, slot / kBlock,
-                                                   slot % kBlock, h, Hkv, lane, ksc, vsc);
-                }
-            }
-        } else {
+        if (!listed_appends) {
             for_each_append([&](int r, int h, int slot) {
                 const long row = ((long)r * Hkv + h) * D * IB;
                 float ksc, vsc;
@@ -904,7 +884,57 @@ void decode_kernel(DecodeArgs a) {
         }
         typename Ops::Regs ra, rb;
         // tile i is computed while tile i + 1 is in flight
-        issue(ra, std::true_type{});
+        if (listed_appends && plan_apps > 0) {
+            // The plan's list: every row's loads go out first, then the first
+            // tile's K/V loads unless that tile is the last of a listed (row,
+            // KV head) -- the one holding its new token -- then the stores.
+            // D / 8 lanes carry one token, so a register set holds 512 / D.
+            constexpr int CPT = D / 8, TPP = kWave / CPT;
+            constexpr int NP = (kPlanMaxAppends + TPP - 1) / TPP;
+            TokenChunk<KIND> tok[NP];
+            int t_rh[NP], t_slot[NP];
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int ti = j * TPP + lane / CPT;
+                int rh = plan_app_rh[0], slot = -1;
+#pragma unroll
+                for (int i = 0; i < kPlanMaxAppends; ++i)
+                    if (i == ti && i < plan_apps) {
+                        rh = plan_app_rh[i];
+                        slot = plan_app_slot[i];
+                    }
+                t_rh[j] = rh;
+                t_slot[j] = slot;
+                const long row = (long)rh * D * IB;
+                tok[j] = load_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
+                                                   static_cast<const char*>(a.v_new) + row,
+                                                   lane % CPT);
+            }
+            auto store_all = [&]() {
+#pragma unroll
+                for (int j = 0; j < NP; ++j) {
+                    if (j * TPP >= plan_apps) break;
+                    const int h = t_rh[j] % Hkv, slot = t_slot[j];
+                    if (slot >= 0) {
+                        float ksc, vsc;
+                        scales(h, ksc, vsc);
+                        store_token_chunk<KIND, D>(tok[j], a.k_cache_w, a.v_cache_w, slot / kBlock,
+                                                   slot % kBlock, h, Hkv, lane % CPT, ksc, vsc);
+                    }
+                }
+            };
+            bool first_holds = false;
+            if (cc.p + 1 == cc.n && cc.jj + 1 == cc.nti) {
+#pragma unroll
+                for (int i = 0; i < kPlanMaxAppends; ++i)
+                    first_holds |= i < plan_apps && plan_app_rh[i] == cc.r * Hkv + cc.h;
+            }
+            if (first_holds) store_all();
+            issue(ra, std::true_type{});
+            if (!first_holds) store_all();
+        } else {
+            issue(ra, std::true_type{});
+        }
         while (true) {
             if (nloaded < ntiles) {
                 issue(rb, std::false_type{});
