@@ -6,7 +6,11 @@
 // at warm-up.  Here the scale is one fp32 value per KV head (K and V apart).
 //
 // One thread moves 8 consecutive head_dim elements of one (token, head)
-// (write_token_chunk in pa_write.hpp: layouts and fp8 encoding).
+// (write_token_chunk in pa_write.hpp: layouts and fp8 encoding).  Lanes run
+// over 16 consecutive tokens first: V is stored token-minor (a block's 16
+// tokens of one dimension are adjacent), so the V stores of one instruction
+// for tokens that fill consecutive slots fall into one 16-byte row -- one
+// memory request instead of sixteen.  Then over 4 chunks of the same tokens.
 #include "pa_internal.hpp"
 #include "pa_write.hpp"
 
@@ -23,12 +27,16 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
                                                      int num_tokens, int num_kv_heads) {
     constexpr int CH = D / 8;                         // 8-element chunks per row
     constexpr int IB = (IN == kF32) ? 4 : 2;          // input element bytes
+    // idx = ((token group * heads + h) * CH / 4 + chunk group) * 64 + 16 c_lo + t_lo
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long total = (long)num_tokens * num_kv_heads * CH;
-    if (idx >= total) return;
-    const int c = (int)(idx % CH);
-    const int h = (int)((idx / CH) % num_kv_heads);
-    const long t = idx / ((long)CH * num_kv_heads);
+    const int lane = (int)(idx & 63);
+    const long rest = idx >> 6;
+    const int cg = (int)(rest % (CH / 4));
+    const int h = (int)((rest / (CH / 4)) % num_kv_heads);
+    const long tg = rest / ((long)(CH / 4) * num_kv_heads);
+    const long t = tg * 16 + (lane & 15);
+    const int c = cg * 4 + (lane >> 4);
+    if (t >= num_tokens) return;
     const int slot = slots[t];
     if (slot < 0) return;
     const long row = (t * num_kv_heads + h) * D * IB;
@@ -43,7 +51,7 @@ template <int IN, int CACHE, int D>
 static hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                 const float* k_scale, const float* v_scale, const int32_t* slots,
                                 int num_tokens, int num_kv_heads, hipStream_t stream) {
-    const long total = (long)num_tokens * num_kv_heads * (D / 8);
+    const long total = (long)((num_tokens + 15) / 16) * 16 * num_kv_heads * (D / 8);
     const long blocks = (total + 255) / 256;
     if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((append_kernel<IN, CACHE, D>), dim3((unsigned)blocks), dim3(256), 0, stream,

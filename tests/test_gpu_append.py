@@ -74,3 +74,32 @@ def test_append_of_zero_tokens_is_a_no_op():
     pa_kv_append(e, e, pool.k, pool.v, i32(np.zeros(0)))
     torch.cuda.synchronize()
     assert host(pool.k).tobytes() == before.tobytes()
+
+
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_of_a_contiguous_run_is_bit_exact(cache, d):
+    """A prefill chunk's tokens: 101 consecutive slots starting at offset 10
+    of a block (groups of 16 tokens straddle two blocks), then 7 scattered
+    ones; bit-exact against the oracle."""
+    rng = np.random.default_rng(7 + d)
+    nb, hkv = 12, 2
+    scales = np.array([0.013, 0.006], np.float32) if cache == "fp8" else None
+    pool = KVPool(nb, hkv, d, cache, k_scale=scales, v_scale=scales[::-1].copy() if scales is not None else None)
+    _random_pool_bytes(pool, rng)
+    k_before, v_before = host(pool.k).copy(), host(pool.v).copy()
+    run = np.arange(16 * 2 + 10, 16 * 2 + 10 + 101)
+    rest = rng.choice(np.setdiff1d(np.arange(nb * 16), run), size=7, replace=False)
+    slots = np.concatenate([run, rest]).astype(np.int32)
+    T = len(slots)
+    in_dt = torch.float32 if cache == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(3 * d)
+    kn = torch.randn(T, hkv, d, generator=g).to(in_dt)
+    vn = torch.randn(T, hkv, d, generator=g).to(in_dt)
+    pa_kv_append(kn.cuda(), vn.cuda(), pool.k, pool.v, i32(slots), pool.k_scale, pool.v_scale)
+    torch.cuda.synchronize()
+    in_name = "f32" if cache == "f32" else "bf16"
+    k_ref, v_ref = opa.oracle_append(k_before, v_before, host(kn), host(vn), slots, in_name, cache,
+                                     scales, None if scales is None else scales[::-1].copy())
+    assert host(pool.k).tobytes() == k_ref.tobytes()
+    assert host(pool.v).tobytes() == v_ref.tobytes()
