@@ -160,6 +160,84 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out
     }
 }
 
+// Up to 256 partitions: one workgroup of four wavefronts per (sequence,
+// query head).  Wavefront w takes partitions w, w + 4, w + 8, .. (lane j holds
+// partition w + 4j's (m, l)) and reduces them as reduce_wave_kernel does,
+// with all of its rows loaded in one round trip (U >= its partition count);
+// the four (max, weight sum, sums) are then combined through LDS.
+template <int D, bool OUT_BF16, int U>
+__global__ __launch_bounds__(256) void reduce_wave4_kernel(void* __restrict__ out,
+                                                           const float* __restrict__ part_max,
+                                                           const float* __restrict__ part_sum,
+                                                           const float* __restrict__ part_out,
+                                                           const int32_t* __restrict__ context_lens,
+                                                           int num_heads, int partition_size,
+                                                           int max_partitions) {
+    constexpr int C = D / kWave;                       // columns per lane
+    __shared__ float s_m[4], s_w[4];
+    __shared__ float s_acc[4][D];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int bh = blockIdx.x;
+    const int b = bh / num_heads;
+    const int L = context_lens[b];
+    const int P = min((L + partition_size - 1) / partition_size, max_partitions);
+    const long base = (long)bh * max_partitions;
+    const int n = P > wave ? (P - wave + 3) / 4 : 0;   // this wave's partitions
+    // unconditional loads at indices clamped into the caller's buffer
+    const int pl = min(wave + 4 * lane, max_partitions - 1);
+    const float m_raw = part_max[base + pl], l_raw = part_sum[base + pl];
+    const float* po = part_out + base * D + C * lane;
+    float row[U][C];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+            row[u][k] = po[(long)min(wave + 4 * u, max_partitions - 1) * D + k];
+    __builtin_amdgcn_sched_barrier(0);          // all of them out before the first wait
+    const float mp = lane < n ? m_raw : -INFINITY;
+    const float M = wave_max(mp);
+    const float w = lane < n ? l_raw * fast_exp2((mp - M) * kLog2e) : 0.f;
+    const float W = wave_sum(w);
+    float acc[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float wp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                       __builtin_bit_cast(int, w), u));
+#pragma unroll
+        for (int k = 0; k < C; ++k) acc[k] += (u < n) ? wp * row[u][k] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < C; ++k) s_acc[wave][C * lane + k] = acc[k];
+    if (lane == 0) {
+        s_m[wave] = M;
+        s_w[wave] = W;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const float Mg = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float a[4], Wg = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        a[v] = s_m[v] == -INFINITY ? 0.f : fast_exp2((s_m[v] - Mg) * kLog2e);
+        Wg += a[v] * s_w[v];
+    }
+    const float inv = P > 0 ? 1.0f / Wg : 0.f;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+        float x = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x += a[v] * s_acc[v][C * lane + k];
+        x *= inv;
+        if (OUT_BF16)
+            static_cast<uint16_t*>(out)[(long)bh * D + C * lane + k] = f32_to_bf16_bits(x);
+        else
+            static_cast<float*>(out)[(long)bh * D + C * lane + k] = x;
+    }
+}
+
 template <int D, bool OUT_BF16>
 static hipError_t launch_reduce(void* out, const float* pm, const float* ps, const float* po,
                                 const int32_t* lens, int batch, int num_heads, int partition_size,
@@ -176,6 +254,13 @@ static hipError_t launch_reduce(void* out, const float* pm, const float* ps, con
         else if (max_partitions <= 8) PA_REDUCE_WAVE(8);
         else PA_REDUCE_WAVE(16);
 #undef PA_REDUCE_WAVE
+    } else if (max_partitions <= 4 * kWave) {
+#define PA_REDUCE_WAVE4(UU)                                                                   \
+    hipLaunchKernelGGL((reduce_wave4_kernel<D, OUT_BF16, UU>), dim3((unsigned)pairs), dim3(256), \
+                       0, stream, out, pm, ps, po, lens, num_heads, partition_size, max_partitions)
+        if (max_partitions <= 128) PA_REDUCE_WAVE4(32);
+        else PA_REDUCE_WAVE4(64);
+#undef PA_REDUCE_WAVE4
     } else {
         hipLaunchKernelGGL((reduce_kernel<D, OUT_BF16>), dim3((unsigned)pairs), dim3(256), 0,
                            stream, out, pm, ps, po, lens, num_heads, partition_size,

@@ -76,9 +76,13 @@ def test_split_k_partials_and_reduce(cache, ps):
     assert np.max(np.abs(go[valid] - o[valid])) <= tol
 
 
-def test_reduce_kernel_on_oracle_partials():
-    rng = np.random.default_rng(5)
-    B, hq, d, PS = 6, 8, 128, 64
+@pytest.mark.parametrize("PS", [64, 32, 16, 8])
+def test_reduce_kernel_on_oracle_partials(PS):
+    """Up to 64 partitions one wavefront per (sequence, head) reduces; up to
+    128 and 256 four wavefronts do (32 / 64 rows each); beyond that the
+    general kernel."""
+    rng = np.random.default_rng(5 + PS)
+    B, hq, d = 6, 8, 128
     lens = np.array([0, 1, 64, 65, 700, 4096], np.int32)
     pmax = -(-int(lens.max()) // PS)
     m = rng.normal(0, 3, (B, hq, pmax))
