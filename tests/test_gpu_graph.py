@@ -67,3 +67,90 @@ def test_graph_replays_equal_eager(cache):
         # unrelated eager work between replays
         x = torch.randn(1024, 1024, device="cuda")
         (x @ x).sum().item()
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_two_stream_graph_replays_equal_serial_eager(cache):
+    """The mixed step with the prefill forked onto a second stream after the
+    append and joined before the step ends (decode + reduce on the first):
+    every replay, and an eager two-stream run, equal the serial eager step
+    bit for bit, with a later step's append ordered after the join."""
+    w = build_workload("g2", seed=37, device="cuda", cache_dtype=cache, num_heads=32,
+                       num_kv_heads=8, head_dim=128, decode_lens=[5, 900, 3000, 64, 1],
+                       prefill_chunks=[(200, 300), (0, 96)])
+    pool = gpu_pool(w)
+    ps = 256
+    q = w.q.contiguous()
+    B, hq, d = q.shape
+    pmax = w.max_partitions(ps)
+    pm = torch.empty((B, hq, pmax), device="cuda")
+    psum = torch.empty_like(pm)
+    po = torch.empty((B, hq, pmax, d), device="cuda")
+    out = torch.empty_like(q)
+    qp = w.q_prefill.contiguous()
+    outp = torch.empty_like(qp)
+    lens, bt = i32(w.context_lens), i32(w.block_tables)
+    qsl, cbt, clens = i32(w.query_start_loc), i32(w.chunk_block_tables), i32(w.chunk_context_lens)
+    nk, nv, ns = w.new_k.contiguous(), w.new_v.contiguous(), i32(w.new_slots)
+    side = torch.cuda.Stream()
+
+    def decode_reduce():
+        pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
+                  partition_size=ps, max_partitions=pmax, part_max=pm, part_sum=psum,
+                  part_out=po)
+        pa_decode_splitk_reduce(out, pm, psum, po, lens, ps)
+
+    def prefill():
+        pa_prefill_chunk(outp, qp, qsl, 300, pool.k, pool.v, cbt, clens, w.scale, pool.k_scale,
+                         pool.v_scale)
+
+    def serial_step():
+        pa_kv_append(nk, nv, pool.k, pool.v, ns, pool.k_scale, pool.v_scale)
+        decode_reduce()
+        prefill()
+
+    def forked_step():
+        pa_kv_append(nk, nv, pool.k, pool.v, ns, pool.k_scale, pool.v_scale)
+        # the current stream: under capture, the capturing one
+        main = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            prefill()
+        join = torch.cuda.Event()
+        join.record(side)
+        decode_reduce()
+        main.wait_event(join)
+
+    serial_step()
+    torch.cuda.synchronize()
+    ref, refp = out.clone(), outp.clone()
+    kref, vref = pool.k.clone(), pool.v.clone()
+
+    def check(what):
+        assert torch.equal(out, ref), "decode output differs: %s" % what
+        assert torch.equal(outp, refp), "prefill output differs: %s" % what
+        assert torch.equal(pool.k.view(torch.uint8), kref.view(torch.uint8))
+        assert torch.equal(pool.v.view(torch.uint8), vref.view(torch.uint8))
+
+    out.fill_(float("nan"))
+    outp.fill_(float("nan"))
+    forked_step()
+    torch.cuda.synchronize()
+    check("eager two-stream step")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forked_step()
+        forked_step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        outp.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check("replay %d" % rep)
+        x = torch.randn(1024, 1024, device="cuda")
+        (x @ x).sum().item()
