@@ -164,7 +164,9 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(void* __restrict__ out
 // query head).  Wavefront w takes partitions w, w + 4, w + 8, .. (lane j holds
 // partition w + 4j's (m, l)) and reduces them as reduce_wave_kernel does,
 // with all of its rows loaded in one round trip (U >= its partition count);
-// the four (max, weight sum, sums) are then combined through LDS.
+// the four (max, weight sum, sums) are then combined through LDS.  Row
+// indices are clamped to the sequence's own last partition, so the loads
+// past it (U is sized for the longest sequence) re-read a cached row.
 template <int D, bool OUT_BF16, int U>
 __global__ __launch_bounds__(256) void reduce_wave4_kernel(void* __restrict__ out,
                                                            const float* __restrict__ part_max,
@@ -184,8 +186,9 @@ __global__ __launch_bounds__(256) void reduce_wave4_kernel(void* __restrict__ ou
     const int P = min((L + partition_size - 1) / partition_size, max_partitions);
     const long base = (long)bh * max_partitions;
     const int n = P > wave ? (P - wave + 3) / 4 : 0;   // this wave's partitions
-    // unconditional loads at indices clamped into the caller's buffer
-    const int pl = min(wave + 4 * lane, max_partitions - 1);
+    // unconditional loads at indices clamped to this wave's last partition
+    const int last = max(min(wave + 4 * (n - 1), max_partitions - 1), 0);
+    const int pl = min(wave + 4 * lane, last);
     const float m_raw = part_max[base + pl], l_raw = part_sum[base + pl];
     const float* po = part_out + base * D + C * lane;
     float row[U][C];
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void reduce_wave4_kernel(void* __restrict__ ou
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int k = 0; k < C; ++k)
-            row[u][k] = po[(long)min(wave + 4 * u, max_partitions - 1) * D + k];
+            row[u][k] = po[(long)min(wave + 4 * u, last) * D + k];
     __builtin_amdgcn_sched_barrier(0);          // all of them out before the first wait
     const float mp = lane < n ? m_raw : -INFINITY;
     const float M = wave_max(mp);
