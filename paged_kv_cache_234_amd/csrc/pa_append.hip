@@ -37,14 +37,24 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k_
     const long t = tg * 16 + (lane & 15);
     const int c = cg * 4 + (lane >> 4);
     if (t >= num_tokens) return;
-    const int slot = slots[t];
-    if (slot < 0) return;
+    // the row, the slot and the scales go out together: one memory round
+    // trip before the stores instead of two (slot, then row)
     const long row = (t * num_kv_heads + h) * D * IB;
+    const TokenChunk<CACHE> tok = load_token_chunk<CACHE, D>(static_cast<const char*>(k_new) + row,
+                                                             static_cast<const char*>(v_new) + row, c);
+    int slot = slots[t];
     const float ksc = CACHE == kFP8 ? k_scale[h] : 1.0f;
     const float vsc = CACHE == kFP8 ? v_scale[h] : 1.0f;
-    write_token_chunk<CACHE, D>(static_cast<const char*>(k_new) + row,
-                                static_cast<const char*>(v_new) + row, k_cache, v_cache,
-                                slot / kBlock, slot % kBlock, h, num_kv_heads, c, ksc, vsc);
+    // The slot is tested only after every load has been issued: the empty
+    // asm takes the row and the scales and hands the slot on, so the test
+    // cannot be scheduled between the loads (left to itself the compiler
+    // tests the slot first and sinks the row loads below the test, after
+    // the slot's round trip).
+    asm volatile("" : "+v"(slot) : "v"(tok.k[0]), "v"(tok.v[0]), "v"(tok.k[tok.N - 1]),
+                 "v"(tok.v[tok.N - 1]), "v"(ksc), "v"(vsc));
+    if (slot < 0) return;
+    store_token_chunk<CACHE, D>(tok, k_cache, v_cache, slot / kBlock, slot % kBlock, h,
+                                num_kv_heads, c, ksc, vsc);
 }
 
 template <int IN, int CACHE, int D>
