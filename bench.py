@@ -34,7 +34,13 @@ HBM_PEAK_GBPS = 8000.0
 # model step for all its layers: one pa_decode_plan per PLAN_LAYERS
 # layer-steps (32 is Llama-3-8B's layer count; Qwen2.5-3B has 36).
 PLAN_LAYERS = 32
-DEFAULT_PS = {1: 64, 2: 256, 3: 256, 4: 512, 5: 256}
+# split-K partition per workload: 256 for bf16 sequence batches (8 tiles of
+# 32 tokens per item; the prefix-shared batch also needs its 256-token prefix
+# to be whole partitions), 512 for the long-context batch (its definition),
+# 1024 for the fp8 mixed batch (16 tiles of 64 tokens per item: at 256 the
+# per-item cost of 4-tile items dominates), 512 for draft verification
+DEFAULT_PS = {1: 64, 2: 256, 3: 256, 4: 512, 5: 1024}
+SPEC_VERIFY_PS = 512
 
 
 def parse():
@@ -86,7 +92,7 @@ def main():
     spec = args.workload == "spec-verify"
     if spec:
         w = make_spec_verify(device=dev) if args.seed is None else make_spec_verify(args.seed, dev)
-        ps = 256 if args.partition_size is None else args.partition_size
+        ps = SPEC_VERIFY_PS if args.partition_size is None else args.partition_size
         if ps <= 0:
             raise SystemExit("the draft-verification step is split-K only (--partition-size > 0)")
     else:

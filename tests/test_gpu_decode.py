@@ -57,7 +57,7 @@ def test_edge_lengths_all_groups(cache, hq, hkv, d):
     _check(w, 0)
 
 
-@pytest.mark.parametrize("ps", [16, 48, 64, 128, 512])
+@pytest.mark.parametrize("ps", [16, 48, 64, 128, 512, 1024])
 @pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
 def test_split_k_partials_and_reduce(cache, ps):
     q_dtype = "f32" if cache == "f32" else "bf16"
@@ -168,7 +168,7 @@ def test_shared_prefix_blocks_equal_private_copies_bit_exact(cache):
 
 # ---- the full-size workloads, in the launch configuration the bench times --------
 
-BENCH_PS = {2: 256, 3: 256, 4: 512, 5: 256}
+BENCH_PS = {2: 256, 3: 256, 4: 512, 5: 1024}
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
@@ -179,6 +179,16 @@ def test_full_size_config_sampled_rows(cfg):
     seqs = sorted(set([0, B - 1, int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))] +
                       list(rng.choice(B, size=min(B, 4 if cfg == 4 else 6), replace=False))))
     _check(w, BENCH_PS[cfg], seqs=seqs)
+
+
+def test_full_size_mixed_fp8_at_256_token_partitions():
+    """The mixed fp8 batch's decode rows at the partition size it ran with
+    before (4-tile items), on sampled sequences."""
+    w = make_config(5, device="cuda")
+    rng = np.random.default_rng(55)
+    B = w.batch
+    seqs = sorted(set([0, B - 1] + list(rng.choice(B, size=4, replace=False))))
+    _check(w, 256, seqs=seqs)
 
 
 @pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])

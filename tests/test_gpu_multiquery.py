@@ -65,7 +65,7 @@ def test_multi_query_matches_oracle_all_group_sizes(cache, hq, hkv, d):
     _check(w, 64)
 
 
-@pytest.mark.parametrize("ps", [16, 32, 256])
+@pytest.mark.parametrize("ps", [16, 32, 256, 512])
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
 def test_multi_query_partition_sizes(cache, ps):
     w = _case(cache, 8, 2, 128, CHUNKS, seed=ps)
@@ -99,7 +99,7 @@ def test_spec_verify_workload_full_size():
     oracle on every eighth sequence."""
     w = make_spec_verify(device="cuda")
     pool = gpu_pool(w)
-    out, _, _ = run_multi(w, pool, 256)
+    out, _, _ = run_multi(w, pool, 512)          # the bench's partition size
     torch.cuda.synchronize()
     chunks = list(range(0, w.num_chunks, 8))
     kp, vp = oracle_pool(w, chunks=chunks)
@@ -123,8 +123,8 @@ def test_planned_multi_query_matches_oracle(cache, hq, hkv, d):
 def test_planned_spec_verify_full_size_repeats_exactly():
     w = make_spec_verify(device="cuda")
     pool = gpu_pool(w)
-    out1, _, _ = run_multi(w, pool, 256, planned=True)
-    out2, _, _ = run_multi(w, pool, 256, planned=True)
+    out1, _, _ = run_multi(w, pool, 512, planned=True)
+    out2, _, _ = run_multi(w, pool, 512, planned=True)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
     want, _, _ = run_multi(w, pool, 256)
