@@ -360,10 +360,12 @@ void prefill_lds_kernel(PrefillArgs a) {
         const long phys = load_invariant(bt + __builtin_amdgcn_readfirstlane(lb));
         const char* kb = kbase + phys * blk_stride;
         const char* vb = vbase + phys * blk_stride;
+        // ordinary (temporal) loads: the row groups of one (chunk, KV head)
+        // run on one XCD and read the same blocks, so L2 should keep them
 #pragma unroll
         for (int u = 0; u < NLD; ++u) {
-            sk[u] = load16(kb + 16 * (lane + kWave * u));
-            sv[u] = load16(vb + 16 * (lane + kWave * u));
+            sk[u] = load16_cached(kb + 16 * (lane + kWave * u));
+            sv[u] = load16_cached(vb + 16 * (lane + kWave * u));
         }
     };
     // token tok of the staged block: key 16 (wave & 1) + tok of half wave >> 1
