@@ -453,39 +453,50 @@ def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes):
     kp = np.zeros(shape_k, st)
     vp = np.zeros(shape_v, st)
     qh = raw(w.q_prefill if chunks_only else w.q)
-    done, tokens, elapsed = [], 0, 0.0
-    for b in order:
-        n = -(-int(lens_of[b]) // w.block_size)
-        blocks = tables_of[b, :n].astype(np.int64)
-        sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
-        idx = torch.as_tensor(sel, device=w.fill_k.device)
-        kp, vp = opa.oracle_append(kp, vp, raw(w.fill_k[idx]), raw(w.fill_v[idx]),
-                                   w.fill_slots[sel], w.in_dtype, w.cache_dtype, w.k_scale,
-                                   w.v_scale, w.block_size)
-        t = time.perf_counter()
-        if chunks_only:
-            opa.oracle_prefill(qh, w.q_dtype, w.query_start_loc, kp, vp, w.cache_dtype,
-                               w.chunk_block_tables, w.chunk_context_lens, w.scale, w.k_scale,
-                               w.v_scale, w.block_size, chunks=[int(b)])
-        else:
-            opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables, w.context_lens,
-                              w.scale, w.k_scale, w.v_scale, w.block_size, seqs=[int(b)])
-        elapsed += time.perf_counter() - t
-        done.append(int(b))
-        tokens += int(lens_of[b])
-        if elapsed >= budget_s:
-            break
+    # The first pass fills the oracle's pool sequence by sequence (untimed)
+    # and times each sequence; when the whole workload takes less than the
+    # budget, further passes over the same pool repeat the timed part.
+    done, tokens, elapsed, passes = [], 0, 0.0, 0
+    while elapsed < budget_s:
+        for b in order:
+            if passes == 0:
+                n = -(-int(lens_of[b]) // w.block_size)
+                blocks = tables_of[b, :n].astype(np.int64)
+                sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
+                idx = torch.as_tensor(sel, device=w.fill_k.device)
+                kp, vp = opa.oracle_append(kp, vp, raw(w.fill_k[idx]), raw(w.fill_v[idx]),
+                                           w.fill_slots[sel], w.in_dtype, w.cache_dtype,
+                                           w.k_scale, w.v_scale, w.block_size)
+            elif int(b) not in done_set:
+                continue
+            t = time.perf_counter()
+            if chunks_only:
+                opa.oracle_prefill(qh, w.q_dtype, w.query_start_loc, kp, vp, w.cache_dtype,
+                                   w.chunk_block_tables, w.chunk_context_lens, w.scale, w.k_scale,
+                                   w.v_scale, w.block_size, chunks=[int(b)])
+            else:
+                opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                                  w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size,
+                                  seqs=[int(b)])
+            elapsed += time.perf_counter() - t
+            if passes == 0:
+                done.append(int(b))
+            tokens += int(lens_of[b])
+            if elapsed >= budget_s:
+                break
+        passes += 1
+        done_set = set(done)
     kv = tokens * w.kv_bytes_per_token()
     return {
         "value": round(kv / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": "fp64 oracle %s of %d of %d %s (%d context tokens, %.1f s), "
+        "sample": "fp64 oracle %s of %d of %d %s, %d pass(es) (%d context tokens, %.1f s), "
                   "host affinity %d cores" % ("causal chunks" if chunks_only else "decode",
                                               len(done), n_units,
                                               "sequences' query tokens" if chunks_only else
-                                              "sequences", tokens, elapsed,
+                                              "sequences", passes, tokens, elapsed,
                                               len(os.sched_getaffinity(0))),
         "seconds": round(elapsed, 3),
         "gpu_over_cpu": round((gpu_bytes / (gpu_ms * 1e-3)) / (kv / elapsed), 1)
