@@ -457,7 +457,7 @@ def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes):
     # and times each sequence; when the whole workload takes less than the
     # budget, further passes over the same pool repeat the timed part.
     done, tokens, elapsed, passes = [], 0, 0.0, 0
-    while elapsed < budget_s:
+    while elapsed < budget_s or not done:          # at least one sequence
         for b in order:
             if passes == 0:
                 n = -(-int(lens_of[b]) // w.block_size)

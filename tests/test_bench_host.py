@@ -1,0 +1,61 @@
+"""Host-side logic of bench.py, on the CPU: the oracle baseline's sampling
+and the lookup of measured HBM traffic under profiles/."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bench
+from workloads import make_config
+
+
+def test_cpu_baseline_repeats_passes_until_the_budget():
+    """A workload shorter than the budget is timed over repeated passes, and
+    every pass counts all of its context tokens."""
+    w = make_config(1, device="cpu")
+    r = bench.cpu_baseline(w, 0.5, 0.01, 441344)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] >= 1
+    assert r["seconds"] >= 0.5
+    passes = int(r["sample"].split(" pass(es)")[0].rsplit(" ", 1)[1])
+    assert passes >= 2
+    ctx = int(np.sum(w.context_lens))
+    tokens = int(re.search(r"\((\d+) context tokens", r["sample"]).group(1))
+    # whole passes plus a prefix of the last one
+    assert (passes - 1) * ctx < tokens <= passes * ctx
+    assert r["value"] == pytest.approx(tokens * w.kv_bytes_per_token() / r["seconds"] / 1e9,
+                                       rel=1e-2)
+
+
+def test_cpu_baseline_stops_inside_a_pass_when_the_budget_is_spent():
+    w = make_config(1, device="cpu")
+    r = bench.cpu_baseline(w, 0.0, 0.01, 441344)
+    assert " 1 pass(es)" in r["sample"]
+    assert r["sample"].startswith("fp64 oracle decode of 1 of 4 sequences")
+
+
+@pytest.mark.parametrize("workload,ps,entry", [
+    ("qwen2.5-3b-bf16-decode-b64", 256, "pa_decode_append"),
+    ("llama3-8b-bf16-decode-prefix-shared-b256", 256, "pa_decode_cascade"),
+    ("long-context-bf16-splitk-b8", 512, "pa_decode_append"),
+    ("mixed-chunked-prefill-fp8kv", 1024, "pa_decode_append"),
+    ("qwen2.5-3b-bf16-spec-verify-b64", 512, "pa_decode_multi"),
+])
+def test_every_bench_workload_has_measured_traffic_for_the_current_sources(workload, ps, entry):
+    """profiles/ holds a copy-calibrated FETCH_SIZE + WRITE_SIZE summary for
+    each workload at the partition size the bench uses, taken from the
+    decode sources as they stand (a kernel change makes this fail until the
+    counters are taken again)."""
+    t = bench.measured_traffic(workload, ps, entry)
+    assert t is not None and t > 0
+
+
+def test_traffic_lookup_refuses_other_partitions_and_entries():
+    assert bench.measured_traffic("qwen2.5-3b-bf16-decode-b64", 128, "pa_decode_append") is None
+    assert bench.measured_traffic("qwen2.5-3b-bf16-decode-b64", 256, "pa_decode") is None
+
+
+def test_bench_defaults_match_the_summaries():
+    assert bench.DEFAULT_PS[5] == 1024 and bench.SPEC_VERIFY_PS == 512
+    assert os.path.isdir(os.path.join(bench.ROOT, "profiles"))
