@@ -31,7 +31,12 @@
  *                            chunks gives the one-shot result; llm-infer,
  *                            "What It Does": prefill of ragged batches).
  *
- * Conventions (the pages leave these open; the library fixes them):
+ * Conventions (the pages leave these open; the library fixes them).  The
+ * pool layout below departs from the plainest reading, one [bs][D] tile per
+ * (block, KV head) for K and for V: K keeps the 16 tokens of each 16-byte run
+ * of head dims together, and V is stored token-minor.  Both make the MFMA
+ * operand of a tile one contiguous 16-byte load per lane; the price is that
+ * appending one token writes 16-byte pieces spread over its tile.
  *
  *   block size   bs = 16 tokens.  Slot s = block * bs + offset.
  *   K pool       [num_blocks][num_kv_heads][head_dim / X][bs][X], X = the
@@ -345,16 +350,34 @@ pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_dtype,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, hipStream_t stream);
 
-/* Static, never NULL. */
+/*
+ * Name of a status code: a static string, never NULL.  Every call above
+ * reports an argument, shape or launch problem as a status the caller can
+ * name, instead of falling back to another path (RustInfer, "Tensor
+ * parallelism": unsupported combinations fail with a clear error rather than
+ * silently falling back; infer-lab, technique table: a feature that is not
+ * available says so, with a reason).
+ */
 const char* pa_status_string(pa_status_t status);
 
-/* Bytes of part_max + part_sum + part_out for a split-K decode (fp32). */
+/*
+ * Bytes of part_max + part_sum + part_out for a split-K decode (fp32):
+ * batch * num_heads * max_partitions * (head_dim + 2) * 4.  The caller
+ * allocates this scratch once and passes it to every layer's launch; the
+ * library allocates no temporary device storage per step (RustInfer,
+ * "Architecture": attention kernels take caller-owned, graph-safe scratch
+ * and allocate nothing themselves).  0 for a negative argument.
+ */
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim,
                                  int32_t max_partitions);
 
-/* Runs a one-wave kernel on the current device and checks its result:
- * PA_ERR_LAUNCH when no gfx950 code object loads (a build for the wrong
- * target must fail loudly, never silently). */
+/*
+ * Runs a one-wave kernel on the current device and checks its result:
+ * PA_ERR_LAUNCH when no gfx950 code object loads.  A build for the wrong
+ * target fails here, loudly, rather than at the first attention call or
+ * silently (RustInfer, "Tensor parallelism": fail instead of silently falling
+ * back).
+ */
 pa_status_t pa_selftest(void);
 
 #ifdef __cplusplus

@@ -424,3 +424,87 @@ def test_gather_refuses_tables_that_do_not_cover_the_context():
     vp = np.zeros((4, 1, 64, BS), np.float32)
     with pytest.raises(ValueError):
         pa.gather_sequence(kp, vp, np.array([1, -1], np.int32), 20, "f32")
+
+
+# ---------------------------------------------------------------------------
+# fp8 pools: the K and V scales (InferX, "The kernels underneath", FP8 KV cache
+# paragraph: per-layer K/V scales; the mixed chunked-prefill workload's
+# per-KV-head absmax/448 scales).  Codes are drawn over every finite E4M3 code,
+# K and V get different scales on every head, and the expected values are
+# dequantised by torch's own float8_e4m3fn conversion, not by oracle.fp8_e4m3.
+# ---------------------------------------------------------------------------
+
+FINITE_E4M3 = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+FP8_K_SCALE = np.array([0.013, 0.0071, 0.029], np.float32)
+FP8_V_SCALE = np.array([0.0047, 0.021, 0.0095], np.float32)
+
+
+def _torch_dequant(codes, scale):
+    """[L, Hkv, D] codes -> float64 values, decode(code) * scale[h], via torch."""
+    v = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+    return (v * torch.from_numpy(scale.astype(np.float64))[None, :, None]).numpy()
+
+
+def fp8_case(rng, lens, hq, hkv, d):
+    """Random finite E4M3 codes for K and V of each sequence, laid out in a pool."""
+    _, _, _, tables, nb = random_case(rng, lens, hq, hkv, d)
+    kc = [FINITE_E4M3[rng.integers(0, len(FINITE_E4M3), (L, hkv, d))] for L in lens]
+    vc = [FINITE_E4M3[rng.integers(0, len(FINITE_E4M3), (L, hkv, d))] for L in lens]
+    return kc, vc, tables, nb
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 3), (12, 3)])
+def test_fp8_decode_matches_sdpa_on_dequantised_arrays(hq, hkv):
+    rng = np.random.default_rng(40 + hq)
+    lens = [17, 40, 77, 130]
+    ks, vs = FP8_K_SCALE[:hkv], FP8_V_SCALE[:hkv]
+    kc, vc, tables, nb = fp8_case(rng, lens, hq, hkv, 64)
+    # scores of O(1): |code| <= 448, so a small query keeps softmax non-degenerate
+    q = (rng.standard_normal((len(lens), hq, 64)) * 0.05).astype(np.float32)
+    kp, vp = layout_pool(kc, vc, tables, nb, "fp8")
+    out = pa.oracle_decode(q, "f32", kp, vp, "fp8", tables, lens, SCALE64, ks, vs)
+    for b, L in enumerate(lens):
+        ref = sdpa_reference(q[b:b + 1], [L - 1], _torch_dequant(kc[b], ks),
+                             _torch_dequant(vc[b], vs), SCALE64)
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_prefill_matches_sdpa_on_dequantised_arrays():
+    rng = np.random.default_rng(44)
+    P, C, hq, hkv = 35, 30, 6, 3
+    L = P + C
+    ks, vs = FP8_K_SCALE[:hkv], FP8_V_SCALE[:hkv]
+    kc, vc, tables, nb = fp8_case(rng, [L], hq, hkv, 64)
+    qp = (rng.standard_normal((C, hq, 64)) * 0.05).astype(np.float32)
+    kp, vp = layout_pool(kc, vc, tables, nb, "fp8")
+    out = pa.oracle_prefill(qp, "f32", [0, C], kp, vp, "fp8", tables, [L], SCALE64, ks, vs)
+    ref = sdpa_reference(qp, list(range(P, P + C)), _torch_dequant(kc[0], ks),
+                         _torch_dequant(vc[0], vs), SCALE64)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_append_then_gather_returns_the_dequantised_codes():
+    """bf16 rows -> oracle_append (fp8) -> gather_sequence equals torch's own
+    float8_e4m3fn round trip of x / scale, times the head's scale, for K and V
+    with different scales."""
+    rng = np.random.default_rng(45)
+    L, nb, hkv, d = 37, 8, 3, 64
+    table = np.array([5, 2, 7], np.int32)
+    g = torch.Generator().manual_seed(45)
+    kn = torch.randn(L, hkv, d, generator=g).bfloat16()
+    vn = torch.randn(L, hkv, d, generator=g).bfloat16()
+    ks = (kn.float().abs().amax(dim=(0, 2)).numpy() / np.float32(448)).astype(np.float32)
+    vs = (vn.float().abs().amax(dim=(0, 2)).numpy() / np.float32(448) * np.float32(1.5)).astype(np.float32)
+    slots = np.array([table[p // BS] * BS + p % BS for p in range(L)], np.int32)
+    kp = np.full((nb, hkv, d // 16, BS, 16), 0x7F, np.uint8)
+    vp = np.full((nb, hkv, d, BS), 0x7F, np.uint8)
+    kbits = kn.view(torch.int16).numpy().view(np.uint16)
+    vbits = vn.view(torch.int16).numpy().view(np.uint16)
+    kp, vp = pa.oracle_append(kp, vp, kbits, vbits, slots, "bf16", "fp8", ks, vs)
+    K, V = pa.gather_sequence(kp, vp, table, L, "fp8", ks, vs)
+
+    def want(x, s):
+        y = torch.from_numpy((x.float().numpy() / s[None, :, None]).astype(np.float32))
+        return _torch_dequant(y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), s)
+    assert np.array_equal(K, want(kn, ks))
+    assert np.array_equal(V, want(vn, vs))

@@ -29,6 +29,9 @@ ATTENTION_PINS = [
     lambda: A.test_append_writes_the_layout_and_nothing_else("f32"),
     A.test_append_fp8_encodes_with_per_head_scale,
     A.test_append_then_gather_roundtrips_values,
+    lambda: A.test_fp8_decode_matches_sdpa_on_dequantised_arrays(6, 3),
+    A.test_fp8_prefill_matches_sdpa_on_dequantised_arrays,
+    A.test_fp8_append_then_gather_returns_the_dequantised_codes,
 ]
 
 FP8_PINS = [
@@ -89,6 +92,19 @@ def _gather_without_v_scale(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_
                        None if vs is None else np.ones_like(vs), block_size)
 
 
+def _gather_without_k_scale(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_size=16):
+    return ORIG_GATHER(k_pool, v_pool, row, L, dt,
+                       None if ks is None else np.ones_like(ks), vs, block_size)
+
+
+def _gather_k_with_v_scale(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_size=16):
+    return ORIG_GATHER(k_pool, v_pool, row, L, dt, vs, vs, block_size)
+
+
+def _gather_v_with_k_scale(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_size=16):
+    return ORIG_GATHER(k_pool, v_pool, row, L, dt, ks, ks, block_size)
+
+
 def _gather_off_by_one_block(k_pool, v_pool, row, L, dt, ks=None, vs=None, block_size=16):
     row = np.asarray(row).copy()
     n = -(-L // block_size)
@@ -127,6 +143,9 @@ ATTENTION_MUTANTS = {
     "max not subtracted": ("attend_rows", _attend_factory(subtract_max=False)),
     "V read with K's layout": ("gather_sequence", _gather_v_like_k),
     "V scale not applied": ("gather_sequence", _gather_without_v_scale),
+    "K scale not applied": ("gather_sequence", _gather_without_k_scale),
+    "K dequantised with V's scale": ("gather_sequence", _gather_k_with_v_scale),
+    "V dequantised with K's scale": ("gather_sequence", _gather_v_with_k_scale),
     "block table entries swapped": ("gather_sequence", _gather_off_by_one_block),
     "combine ignores partition sums": ("oracle_combine", _combine_without_partition_sums),
     "append writes V untransposed": ("oracle_append", _append_v_untransposed),

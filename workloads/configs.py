@@ -21,9 +21,11 @@ The five named workloads mirror the shapes the pages serve:
    sequences with L uniform in [512, 8192] plus 4 prefill chunks of 512 query
    tokens after 0..2048 cached tokens; per-KV-head fp32 scales absmax/448.
 
-Conventions shared with both sides: K pool [NB][Hkv][bs][D], V pool
-[NB][Hkv][D][bs]; slot = block * bs + offset; context lengths include this
-step's token; unused block-table entries are -1.
+Conventions shared with both sides: K pool [NB][Hkv][D/X][bs][X] (X = 16
+bytes of elements: 4 fp32, 8 bf16, 16 fp8), V pool [NB][Hkv][D][bs]
+(token-minor); slot = block * bs + offset; context lengths include this step's
+token; unused block-table entries are -1.  This module draws values and
+structure only and does no attention arithmetic.
 """
 
 from dataclasses import dataclass, field
