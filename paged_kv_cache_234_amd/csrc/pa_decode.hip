@@ -27,10 +27,21 @@
 // an item of an equal share; its NW wavefronts split that run into NW equal
 // runs of tiles.  A wavefront
 // streams its tiles back to back: the next tile's K/V loads -- across item
-// boundaries too -- are in flight while the current tile is multiplied, a
-// finished item writes its partial (or output) straight from registers, and
-// an item cut between wavefronts is merged through LDS by the wavefront that
-// holds its first tile.
+// boundaries too -- are in flight while the current tile is multiplied, and a
+// finished item writes its partial (or output) straight from registers.
+//
+// Items cut between wavefronts.  Every item is computed as one online softmax
+// over its tiles in order, whichever wavefronts hold them, so an item's result
+// does not depend on where the batch around it puts the cuts: a sequence's
+// output is the same, bit for bit, alone or in any batch, and a prefix
+// partition read for a group row equals the one a member's own row reads
+// (infer-lab, invariants: batched decode equals sequential decode, and
+// prefix-cached equals uncached).  A wavefront runs its range in the order
+// Y, M, X: Y = the first tiles of the item cut at its end, M = its whole
+// items, X = the last tiles of the item cut at its start.  After Y it parks
+// its running softmax state in LDS; the next wavefront takes that state when
+// it reaches its X, last, and continues the same softmax from it.  The state
+// is handed on, never merged, so the arithmetic equals one wavefront's.
 #include <algorithm>
 #include <type_traits>
 
@@ -118,8 +129,8 @@ struct DecodeArgs {
 template <int KIND> struct QType { using T = uint16_t; };
 template <> struct QType<kF32> { using T = float; };
 
-// Online-softmax state of one wavefront's piece of an item, parked in LDS
-// until the wavefront owning the item's first tile merges it.
+// Running online-softmax state of an item cut at the end of a wavefront's
+// range, parked in LDS for the wavefront that continues the item.
 template <int NVT, int NC> struct SegSlot {
     f32x4 o[NC][NVT][kWave];
     float m[NC][kWave], mr[NC][kWave], l[NC][kWave];
@@ -161,7 +172,8 @@ void decode_kernel(DecodeArgs a) {
     __shared__ int s_cpre[kCost ? kMaxDecodeRows + 1 : 1];
     __shared__ int s_csum[NW];
     __shared__ int s_wstart[NW + 1];             // the wavefronts' first tiles, then the end
-    __shared__ SegSlot<NVT, NC> s_seg[NW];       // each wave's first piece, if cut
+    __shared__ SegSlot<NVT, NC> s_seg[NW];       // state of the item cut at a wave's end
+    __shared__ int s_ready[NW];                  // s_seg[w] holds it
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -305,8 +317,32 @@ void decode_kernel(DecodeArgs a) {
             }
         }
     };
+    // A plan made for other arguments: the launch computes nothing, and every
+    // element of the output (or of the partial buffers) it was given becomes
+    // NaN, so the mistake cannot pass for a result (RustInfer, "Tensor
+    // parallelism": fail instead of silently falling back).
+    auto poison_outputs = [&]() {
+        // rows of the output / partial buffers: sequences, or multi-query tokens
+        const long rows = multi ? (long)max(0, load_invariant(a.query_start_loc + B)) : (long)B;
+        const long stride = (long)gridDim.x * NT, start = (long)blockIdx.x * NT + tid;
+        if (a.split) {
+            const long n = rows * a.num_heads * a.max_partitions;
+            for (long i = start; i < n; i += stride) {
+                a.part_max[i] = __builtin_nanf("");
+                a.part_sum[i] = __builtin_nanf("");
+            }
+            for (long i = start; i < n * D; i += stride) a.part_out[i] = __builtin_nanf("");
+        } else {
+            const long n = rows * a.num_heads * D;
+            for (long i = start; i < n; i += stride) {
+                if (KIND == kF32) reinterpret_cast<float*>(a.out)[i] = __builtin_nanf("");
+                else reinterpret_cast<uint16_t*>(a.out)[i] = 0x7FC0;
+            }
+        }
+    };
     if constexpr (MODE == kUsePlan) {
-        zero_empty_rows();
+        if (plan_ok) zero_empty_rows();
+        else poison_outputs();
     } else {
     // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
     const int per = (R + NT - 1) / NT;
@@ -485,10 +521,11 @@ void decode_kernel(DecodeArgs a) {
     // rows of this wavefront's first and last tiles
     if (g1 > g0) row_of2(g0, g1 - 1, rg0, rg1);
     }
-    // each wavefront's first tile (and the workgroup's end), for the merge
+    // each wavefront's first tile (and the workgroup's end): a wavefront whose
+    // range starts inside an item finds there the one holding the tile before
     s_wstart[wave] = g0;
     if (wave == NW - 1) s_wstart[NW] = g1;
-    auto wave_start = [&](int w) { return s_wstart[w]; };
+    s_ready[wave] = 0;
     const int ntiles = g1 - g0;
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
@@ -595,17 +632,72 @@ void decode_kernel(DecodeArgs a) {
         return (sq >= 0 && sq < B) ? sq : 0;
     };
 
-    Cursor cc;          // tile being computed
-    if (ntiles > 0) {
-        const int r = rg0;
+    // cursor at tile g of row r
+    auto cursor_at = [&](Cursor& c, int g, int r) __attribute__((always_inline)) {
         const int th = row_head_tiles(r);
         const int base = s_tpre[r];
-        const int vh = (g0 - base) / th;
-        const int j = g0 - base - vh * th;
+        const int vh = (g - base) / th;
+        const int j = g - base - vh * th;
         const int p = j / tpi;
-        set_item(cc, r, vh, p, base + vh * th + p * tpi);
-        cc.jj = j - p * tpi;
+        set_item(c, r, vh, p, base + vh * th + p * tpi);
+        c.jj = j - p * tpi;
+    };
+
+    // ---- the range in processing order: Y, M, X ----------------------------
+    // Y = [yb, g1), the first tiles of the item cut at g1; M = the whole items
+    // between; X = [g0, xa), the last tiles of the item cut at g0.  Y is
+    // computed from the item's start and parked; X continues the state the
+    // wavefront before parked.  A range inside one item cut at both ends is
+    // one segment that takes the state, continues it and parks it.  Segment k
+    // covers tiles [sbk, sek) and starts in row srk.
+    int sb0 = 0, se0 = 0, sr0 = 0, sb1 = 0, se1 = 0, sr1 = 0, sb2 = 0, se2 = 0, sr2 = 0;
+    bool x_cut = false;       // g0 lies inside an item: X waits for the state of its head
+    Cursor cc;                // tile being computed
+    if (ntiles > 0) {
+        Cursor cx, cy;
+        cursor_at(cx, g0, rg0);
+        cursor_at(cy, g1 - 1, rg1);
+        x_cut = cx.jj != 0;
+        const bool y_cut = cy.jj + 1 != cy.nti;
+        const int xa = (int)(cx.t0 + cx.nti), yb = (int)cy.t0;
+        if (x_cut && y_cut && cx.t0 == cy.t0) {
+            sb0 = g0;
+            se0 = g1;
+            sr0 = rg0;
+        } else {
+            // the segments that are not empty, in the order Y, M, X (chosen
+            // by value: stores through a selected pointer would keep them in
+            // scratch memory)
+            const int mb = x_cut ? xa : g0, me = y_cut ? yb : g1;
+            const bool has_m = mb < me;
+            int rm = rg0;
+            if (has_m)
+                while (s_tpre[rm + 1] <= mb) ++rm;        // the row holding tile mb
+            sb0 = y_cut ? yb : has_m ? mb : g0;
+            se0 = y_cut ? g1 : has_m ? me : xa;
+            sr0 = y_cut ? rg1 : has_m ? rm : rg0;
+            sb1 = y_cut && has_m ? mb : g0;
+            se1 = y_cut && has_m ? me : xa;
+            sr1 = y_cut && has_m ? rm : rg0;
+            sb2 = g0;
+            se2 = xa;
+            sr2 = rg0;
+        }
+        cursor_at(cc, sb0, sr0);
     }
+    // move a cursor to the next tile in processing order; s: its segment.
+    // Only called while another tile of this wavefront's range exists.
+    // (by value: a conditional over the captured lvalues would select their
+    // addresses and keep the whole closure in scratch memory)
+    auto pick = [](int k, int v0, int v1, int v2) { return k == 0 ? v0 : k == 1 ? v1 : v2; };
+    auto next_tile = [&](Cursor& c, int& s) __attribute__((always_inline)) {
+        if (c.t0 + c.jj + 1 == pick(s, se0, se1, se2)) {
+            ++s;
+            cursor_at(c, pick(s, sb0, sb1, sb2), pick(s, sr0, sr1, sr2));
+        } else {
+            advance(c);
+        }
+    };
 
     // ---- plan launch: record what this prologue found, then stop ----------
     if constexpr (MODE == kMakePlan) {
@@ -621,7 +713,8 @@ void decode_kernel(DecodeArgs a) {
         if (ntiles > 0) tile_ids(cc, 6);
         if (ntiles > 1) {
             Cursor c1 = cc;
-            advance(c1);
+            int s1 = 0;
+            next_tile(c1, s1);
             tile_ids(c1, 10);
         }
         const int vals[6] = {g0, g1, wg_a, wg_e, rg0, rg1};
@@ -660,8 +753,8 @@ void decode_kernel(DecodeArgs a) {
         }
         return;
     }
-    bool tail_open = false;       // this wave's last piece ends inside its item
-    Cursor tail_item;
+    // every wavefront's s_wstart and cleared s_ready are visible from here on
+    __syncthreads();
 
     WaveSoftmax<KIND, D, NC> st;
     typename Ops::Q qop[NC];
@@ -777,19 +870,59 @@ void decode_kernel(DecodeArgs a) {
             }
         }
     };
-    auto park = [&](SegSlot<NVT, NC>& s) {
+    // Hand the running state of the item cut at this wavefront's end to the
+    // one that continues it.  A wavefront's LDS writes are performed in
+    // order, so once the flag is seen the state is there; the compiler-only
+    // fences keep the stores (and, on the taking side, the loads) on their
+    // side of the flag without waiting for the K/V loads in flight.
+    auto park = [&]() __attribute__((always_inline)) {
+        SegSlot<NVT, NC>& sl = s_seg[wave];
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
 #pragma unroll
-            for (int t = 0; t < NVT; ++t) s.o[n][t][lane] = st.o[n][t];
-            s.m[n][lane] = st.m[n];
-            s.mr[n][lane] = st.mr[n];
-            s.l[n][lane] = st.l[n];
+            for (int t = 0; t < NVT; ++t) sl.o[n][t][lane] = st.o[n][t];
+            sl.m[n][lane] = st.m[n];
+            sl.mr[n][lane] = st.mr[n];
+            sl.l[n][lane] = st.l[n];
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) *static_cast<volatile int*>(&s_ready[wave]) = 1;
+    };
+    // Take the state of the item cut at g0 from the wavefront holding tile
+    // g0 - 1 (the last one before this with a non-empty range; wave 0's range
+    // starts at an item).  That wavefront parks it after the first segment it
+    // computes, which waits on nobody unless it too lies inside this item,
+    // and then on a wavefront before it: the chain ends at the item's head.
+    // The wait is bounded (about two seconds, far beyond any item's time):
+    // should a damaged plan ever send a range into an item nobody parks, the
+    // item comes out NaN instead of the wavefront spinning forever.
+    auto take = [&]() __attribute__((always_inline)) {
+        int from = max(wave - 1, 0);
+        while (from > 0 && s_wstart[from] >= g0) --from;
+        bool ok = from < wave;
+        for (int spin = 0; ok && *static_cast<volatile int*>(&s_ready[from]) == 0; ++spin) {
+            if (spin == (1 << 26)) ok = false;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const SegSlot<NVT, NC>& sl = s_seg[from];
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+                const f32x4 v = sl.o[n][t][lane];
+                st.o[n][t] = ok ? v : f32x4{nan, nan, nan, nan};
+            }
+            st.m[n] = ok ? sl.m[n][lane] : nan;
+            st.mr[n] = ok ? sl.mr[n][lane] : nan;
+            st.l[n] = ok ? sl.l[n][lane] : nan;
         }
     };
 
     if (ntiles > 0) {
         Cursor lc = cc;     // tile being loaded (one ahead)
+        int ls = 0, cs = 0; // segments of the load and compute cursors
         int nloaded = 0;
         int phys[TB];
         const int32_t* bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
@@ -809,7 +942,7 @@ void decode_kernel(DecodeArgs a) {
             for (int j = 0; j < TB; ++j) ph[j] = phys[j];
             if (++nloaded < ntiles) {
                 const int orow = lc.r, ovh = lc.vh;
-                advance(lc);
+                next_tile(lc, ls);
                 if (lc.r != orow)
                     bt = a.block_tables + (long)table_seq(lc.r) * a.max_blocks_per_seq;
                 if constexpr (MODE == kUsePlan && decltype(first)::value) {
@@ -829,7 +962,12 @@ void decode_kernel(DecodeArgs a) {
             Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, ph, lane);
         };
         int ncomputed = 0;
-        bool piece_from_start = cc.jj == 0;
+        // entering a tile: X's first tile takes the parked state, an item's
+        // first tile starts from scratch, any other continues
+        auto enter = [&]() __attribute__((always_inline)) {
+            if (x_cut && cc.t0 + cc.jj == g0) take();
+            else if (cc.jj == 0) st.init();
+        };
         auto compute = [&](typename Ops::Regs& r) {
             const int t0 = cc.tb + cc.jj * TT;
             const int nvalid = cc.te - t0;
@@ -839,34 +977,26 @@ void decode_kernel(DecodeArgs a) {
             st.step(r, qop, c, nvalid, limit, nvalid < TT || t0 + TT - 1 > cc.qmin, lane);
             ++ncomputed;
             const bool item_done = cc.jj + 1 == cc.nti;
-            const bool run_done = ncomputed == ntiles;
-            if (item_done || run_done) {
-                if (piece_from_start && item_done) {
-                    finish_item(cc);
-                } else if (!piece_from_start) {
-                    park(s_seg[wave]);              // continues an item of the previous wave
-                } else {
-                    tail_open = true;               // continued by the next wave(s)
-                    tail_item = cc;
-                }
-                if (!run_done) {
-                    const int orow = cc.r, ovh = cc.vh;
-                    advance(cc);
-                    piece_from_start = true;
-                    st.init();
-                    if (cc.r != orow || cc.vh != ovh) {
-                        if (kPrefetchQ && ++comp_ord == next_ord) {
+            const bool seg_done = cc.t0 + cc.jj + 1 == pick(cs, se0, se1, se2);
+            if (item_done) finish_item(cc);
+            else if (seg_done) park();                  // continued by a later wavefront
+            if (ncomputed == ntiles) return;
+            if (item_done || seg_done) {
+                const int orow = cc.r, ovh = cc.vh;
+                next_tile(cc, cs);
+                enter();
+                if (cc.r != orow || cc.vh != ovh) {
+                    if (kPrefetchQ && ++comp_ord == next_ord) {
 #pragma unroll
-                            for (int n = 0; n < NC; ++n) {
-                                qop[n] = qnext[n];
-                                col_seq[n] = next_seq[n];
-                                col_hq[n] = next_hq[n];
-                                col_last[n] = next_last[n];
-                            }
-                            c = next_c;
-                        } else {
-                            q_for(cc, qop, col_seq, col_hq, col_last, c);
+                        for (int n = 0; n < NC; ++n) {
+                            qop[n] = qnext[n];
+                            col_seq[n] = next_seq[n];
+                            col_hq[n] = next_hq[n];
+                            col_last[n] = next_last[n];
                         }
+                        c = next_c;
+                    } else {
+                        q_for(cc, qop, col_seq, col_hq, col_last, c);
                     }
                 }
             } else {
@@ -874,7 +1004,6 @@ void decode_kernel(DecodeArgs a) {
             }
         };
 
-        st.init();
         q_for(cc, qop, col_seq, col_hq, col_last, c);
         if constexpr (MODE == kUsePlan) {
 #pragma unroll
@@ -935,6 +1064,7 @@ void decode_kernel(DecodeArgs a) {
         } else {
             issue(ra, std::true_type{});
         }
+        enter();
         while (true) {
             if (nloaded < ntiles) {
                 issue(rb, std::false_type{});
@@ -951,31 +1081,6 @@ void decode_kernel(DecodeArgs a) {
                 break;
             }
         }
-    }
-
-    // ---- merge items cut between wavefronts --------------------------------
-    __syncthreads();
-    if (tail_open) {
-        const long item_end = tail_item.t0 + tail_item.nti;
-        for (int w = wave + 1; w < NW; ++w) {
-            const long s0 = wave_start(w), s1 = wave_start(w + 1);
-            if (s0 >= item_end) break;
-            if (s1 == s0) continue;
-            const SegSlot<NVT, NC>& s = s_seg[w];
-#pragma unroll
-            for (int n = 0; n < NC; ++n) {
-                const float mr2 = s.mr[n][lane];
-                const float mnew = fmaxf(st.mr[n], mr2);
-                const float a1 = st.mr[n] == mnew ? 1.f : fast_exp2(st.mr[n] - mnew);
-                const float a2 = mr2 == mnew ? 1.f : fast_exp2(mr2 - mnew);
-                st.mr[n] = mnew;
-                st.m[n] = fmaxf(st.m[n], s.m[n][lane]);
-                st.l[n] = st.l[n] * a1 + s.l[n][lane] * a2;
-#pragma unroll
-                for (int t = 0; t < NVT; ++t) st.o[n][t] = st.o[n][t] * a1 + s.o[n][t][lane] * a2;
-            }
-        }
-        finish_item(tail_item);
     }
 }
 

@@ -90,28 +90,36 @@ def test_cascade_without_groups_is_pa_decode_bit_exact(cache):
         assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
-def test_cascade_agrees_with_pa_decode(cache):
-    w = _case("bf16", cache, 8, 2, 128, seed=12)
+@pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 1), (12, 4)])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_cascade_equals_pa_decode_bit_exact(cache, hq, hkv, planned):
+    """infer-lab: prefix-cached decode == uncached decode, bit for bit.  A
+    shared partition read once for a group's members gives each member the
+    partial its own row would compute, so outputs and partials are equal."""
+    q_dtype = "f32" if cache == "f32" else "bf16"
+    w = _case(q_dtype, cache, hq, hkv, 128, seed=12 + hq)
     pool = gpu_pool(w)
-    out_c, _ = run_cascade(w, pool, 64)
-    out_d, _ = run_decode(w, pool, 64)
+    out_c, parts_c = run_cascade(w, pool, 64, planned=planned)
+    out_d, parts_d = run_decode(w, pool, 64)
     torch.cuda.synchronize()
-    assert max_abs_err(as_f64(out_c), as_f64(out_d)) <= TOL[cache]
+    assert torch.equal(out_c, out_d)
+    for a, b in zip(parts_c, parts_d):
+        assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
 
 
 def test_cascade_full_size_prefix_shared_config():
     """Llama-3-8B-shaped prefix-shared decode at full size (batch 256, groups
     of 8 sharing 16 blocks), partition 256: the oracle on a sample of
-    sequences (every group's first and last member and the longest), pa_decode
-    on all of them."""
+    sequences (every group's first and last member and the longest); equal
+    to pa_decode on all of them, bit for bit."""
     w = make_config(3, device="cuda")
     pool = gpu_pool(w)
     out_c, _ = run_cascade(w, pool, 256)
     out_d, _ = run_decode(w, pool, 256)
     torch.cuda.synchronize()
     tol = TOL[w.cache_dtype]
-    assert max_abs_err(as_f64(out_c), as_f64(out_d)) <= tol
+    assert torch.equal(out_c, out_d)
     seqs = sorted({int(m[0]) for m, _ in w.prefix_groups[::4]} |
                   {int(m[-1]) for m, _ in w.prefix_groups[::4]} |
                   {int(np.argmax(w.context_lens))})

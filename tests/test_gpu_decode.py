@@ -121,10 +121,10 @@ def test_zero_length_sequences_give_zeros(cache, ps):
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
 @pytest.mark.parametrize("ps", [0, 64])
 def test_batched_equals_sequential_and_runs_repeat_bit_exact(cache, ps):
-    """infer-lab: batched decode == sequential decode.  The kernel balances
-    tiles over the whole batch, so the points where a sequence's work is cut
-    between wavefronts depend on the batch: batched and one-by-one results
-    agree within the tolerance, and a repeated call is bit for bit equal."""
+    """infer-lab: batched decode == sequential decode, bit for bit.  Where the
+    batch cuts a sequence's work between wavefronts changes, but each item is
+    one online softmax over its tiles in order whichever wavefronts hold
+    them, so the result does not."""
     w = _case("bf16", cache, 16, 2, 128, [33, 700, 1, 250, 4000], seed=11)
     pool = gpu_pool(w)
     full, _ = run_decode(w, pool, ps)
@@ -133,7 +133,28 @@ def test_batched_equals_sequential_and_runs_repeat_bit_exact(cache, ps):
     for b in range(w.batch):
         one, _ = run_decode(w, pool, ps, q=w.q[b:b + 1], block_tables=w.block_tables[b:b + 1],
                             context_lens=w.context_lens[b:b + 1])
-        assert max_abs_err(as_f64(one[0]), as_f64(full[b])) <= TOL[cache]
+        assert torch.equal(one[0], full[b]), "sequence %d differs alone" % b
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_full_size_batch_invariance_bit_exact(cache):
+    """The Qwen2.5-3B-shaped batch (64 sequences, partition 256): every
+    sequence of the batch equals the same sequence in a batch of its own and
+    in the batch reversed, bit for bit (different cut points each time)."""
+    w = make_config(2, device="cuda")
+    if cache == "fp8":
+        w = _case("bf16", "fp8", 16, 2, 128, list(w.context_lens[:24]), seed=91)
+    pool = gpu_pool(w)
+    ps = 256
+    full, _ = run_decode(w, pool, ps)
+    rev = np.arange(w.batch)[::-1].copy()
+    back, _ = run_decode(w, pool, ps, q=w.q[torch.as_tensor(rev, device="cuda")],
+                         block_tables=w.block_tables[rev], context_lens=w.context_lens[rev])
+    assert torch.equal(back.flip(0), full)
+    for b in [0, 5, int(np.argmax(w.context_lens)), w.batch - 1]:
+        one, _ = run_decode(w, pool, ps, q=w.q[b:b + 1], block_tables=w.block_tables[b:b + 1],
+                            context_lens=w.context_lens[b:b + 1])
+        assert torch.equal(one[0], full[b]), "sequence %d differs alone" % b
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])

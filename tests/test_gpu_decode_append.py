@@ -206,16 +206,24 @@ def test_one_plan_serves_every_layer():
         assert torch.equal(got, want)
 
 
-def test_a_plan_for_other_arguments_does_nothing():
-    """A plan made for another partition size: the launch writes nothing."""
+@pytest.mark.parametrize("plan_ps,ps", [(64, 0), (64, 256), (0, 64)])
+def test_a_plan_for_other_arguments_gives_nan(plan_ps, ps):
+    """A plan made for another partition size: the launch computes and
+    appends nothing, and every element of its output (or partial buffers,
+    hence of the reduced output) is NaN, so the mistake cannot pass for a
+    result."""
     w = build_workload("fw", seed=22, device="cuda", num_heads=16, num_kv_heads=2, head_dim=128,
                        decode_lens=[100, 700, 33])
     pool = gpu_pool(w, without_new=True)
-    before = pool.k.clone()
-    plan = _plan_for(w, pool, 64)
-    got, _ = _run_planned(w, pool, 0, plan, out_fill=3.0)
-    assert torch.all(got == 3.0)
-    assert torch.equal(pool.k.view(torch.uint8), before.view(torch.uint8))
+    before_k, before_v = pool.k.clone(), pool.v.clone()
+    plan = _plan_for(w, pool, plan_ps)
+    got, parts = _run_planned(w, pool, ps, plan, out_fill=3.0)
+    assert torch.all(torch.isnan(got))
+    if ps:
+        for t in parts:
+            assert torch.all(torch.isnan(t))
+    assert torch.equal(pool.k.view(torch.uint8), before_k.view(torch.uint8))
+    assert torch.equal(pool.v.view(torch.uint8), before_v.view(torch.uint8))
 
 
 @pytest.mark.parametrize("cfg,ps", [(2, 256), (4, 512), (1, 0)])
