@@ -1,19 +1,39 @@
-"""Benchmark one paged-attention layer-step on one MI355X.
+"""Benchmark paged-attention layer-steps on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all]
 
-A step is one pass of the whole hot path over one batch: pa_kv_append of the
-step's new tokens, split-K pa_decode, pa_decode_splitk_reduce, and for the
-mixed workload (config 5) pa_prefill_chunk.  Inputs are resident in HBM
-before timing starts.  The pool of every step is a different layer copy
-(rotating over R copies, R * pool >= 1 GiB), so each step reads its KV from
-HBM rather than from the 256 MB Infinity Cache, as a real layer-step does.
+A step is one pass of the whole hot path over one batch: the append of the
+step's new tokens, split-K decode, pa_decode_splitk_reduce, and for the mixed
+workload pa_prefill_chunk.  The default run times every workload, one after
+another in this process:
 
-Prints one JSON line: the headline metric is KV GB/s of the whole step
-(logical KV bytes read / step time), with us per layer-step, the fraction of
-the 8 TB/s HBM peak, per-kernel HIP-event durations, the roofline of the
-decode kernel and the fp64 CPU oracle timed on a bounded sample of the same
-workload.
+  tiny-fp32-decode                          B=4 fp32, D=64 (launch-bound)
+  qwen2.5-3b-bf16-decode-b64                bf16, 16/2 heads (gate config)
+  llama3-8b-bf16-decode-prefix-shared-b256  bf16, 32/8 heads, groups of 8
+                                            sharing 16 blocks (gate config)
+  long-context-bf16-splitk-b8               bf16, 32/8 heads, L in [32k, 128k]
+  mixed-chunked-prefill-fp8kv               fp8 KV, 60 decode + 4 x 512 prefill
+  qwen2.5-3b-bf16-spec-verify-b64           draft verification, 2-8 tokens each
+
+and prints ONE JSON line.  Its headline (value, ms_per_step, config,
+roofline, cpu_baseline) is the long-context batch, the largest workload that
+one GPU holds; "configs" carries the same figures for every workload.
+
+Inputs are resident in HBM before timing starts.  The pool of every step is
+a different layer copy (rotating over R copies, R * pool >= 1 GiB), so each
+step reads its KV from HBM rather than from the 256 MB Infinity Cache, as a
+real layer-step does.  K timed steps are one captured graph, as the pages'
+engines replay their decode step; the decode launches read a plan made once
+per PLAN_LAYERS layer-steps, and each captured region holds its share of
+plan launches (ceil(K / PLAN_LAYERS)).
+
+Per workload: µs per layer-step, KV GB/s (logical KV bytes read / step
+time), the fraction of the 8 TB/s HBM peak on unique KV bytes, per-kernel
+HIP-event durations, the roofline of the decode kernel (algorithmic bytes /
+its duration, HIP events on its launch stream, plus the copy-calibrated HBM
+traffic that profiles/ records for the current decode sources), and the
+fp64 CPU oracle timed on a bounded sample of the same workload, with all the
+host's cores and with one thread.
 """
 
 import argparse
@@ -30,227 +50,306 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-decode KV GB/s (% of HBM peak) + µs per layer-step, 1×MI355X"
 HBM_PEAK_GBPS = 8000.0
-# Plain decode steps read their launch prologue from a plan made once per
-# model step for all its layers: one pa_decode_plan per PLAN_LAYERS
-# layer-steps (32 is Llama-3-8B's layer count; Qwen2.5-3B has 36).
+# Decode launches read their prologue from a plan made once per model step
+# for all its layers: one pa_decode_plan per PLAN_LAYERS layer-steps (32 is
+# Llama-3-8B's layer count; Qwen2.5-3B has 36).
 PLAN_LAYERS = 32
 # split-K partition per workload: 256 for bf16 sequence batches (8 tiles of
 # 32 tokens per item; the prefix-shared batch also needs its 256-token prefix
 # to be whole partitions), 512 for the long-context batch (its definition),
 # 1024 for the fp8 mixed batch (16 tiles of 64 tokens per item: at 256 the
-# per-item cost of 4-tile items dominates), 512 for draft verification
-DEFAULT_PS = {1: 64, 2: 256, 3: 256, 4: 512, 5: 1024}
+# per-item cost of 4-tile items dominates), 512 for draft verification; the
+# tiny fp32 batch uses one-tile items, which no wavefront shares
+DEFAULT_PS = {1: 16, 2: 256, 3: 256, 4: 512, 5: 1024}
 SPEC_VERIFY_PS = 512
+HEADLINE = "long-context-bf16-splitk-b8"
+# the bf16 configs the >= 70 % of HBM peak target applies to
+GATE = ("qwen2.5-3b-bf16-decode-b64", "llama3-8b-bf16-decode-prefix-shared-b256")
 
 
-def parse():
+def plan_due(layer, base):
+    """Whether layer-step `layer` of a region starting at `base` remakes the
+    plan: the region's first step and every PLAN_LAYERS-th after it, so a
+    region of K steps holds ceil(K / PLAN_LAYERS) plan launches."""
+    return (layer - base) % PLAN_LAYERS == 0
+
+
+def workload_names():
+    from workloads import CONFIG_NAMES, SPEC_VERIFY_NAME
+    return [CONFIG_NAMES[i] for i in sorted(CONFIG_NAMES)] + [SPEC_VERIFY_NAME]
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--workload", default=None, choices=["spec-verify"],
-                    help="instead of a numbered config: the draft-verification step "
-                         "(pa_decode_multi over U[2, 8] causal query tokens per sequence)")
+    ap.add_argument("--workload", default="all",
+                    help="all (default), or one workload name: " + ", ".join(workload_names()))
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="one numbered workload (same as --workload <its name>)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-fuse-append", action="store_true",
                     help="append the decode tokens with pa_kv_append before pa_decode instead of "
                          "pa_decode_append's single launch")
     ap.add_argument("--no-plan", action="store_true",
-                    help="plain decode launches compute their prologue instead of reading a "
+                    help="decode launches compute their prologue instead of reading a "
                          "per-step plan")
     ap.add_argument("--no-cascade", action="store_true",
                     help="decode prefix-sharing batches with pa_decode instead of pa_decode_cascade")
     ap.add_argument("--eager", action="store_true",
                     help="launch the kernels one by one instead of replaying captured graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU budget of the oracle baseline")
-    return ap.parse_args()
+    ap.add_argument("--cpu-seconds", type=float, default=None,
+                    help="CPU budget of the oracle baseline per workload, all cores (default "
+                         "3 s per workload when timing all of them, 12 s for one)")
+    ap.add_argument("--cpu-seconds-1t", type=float, default=None,
+                    help="the same with one thread (default half of --cpu-seconds)")
+    args = ap.parse_args(argv)
+    names = workload_names()
+    if args.config is not None:
+        args.workload = names[args.config - 1]
+    if args.workload != "all" and args.workload not in names:
+        ap.error("unknown workload %r" % args.workload)
+    if args.cpu_seconds is None:
+        args.cpu_seconds = 3.0 if args.workload == "all" else 12.0
+    if args.cpu_seconds_1t is None:
+        args.cpu_seconds_1t = args.cpu_seconds / 2
+    return args
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the paged-attention path here is built and timed on "
-              "a single MI355X (no sharding, no collectives); --gpus %d is not supported"
-              % max(args.gpus, world), file=sys.stderr)
-        sys.exit(2)
+def make_workload(name, seed, dev):
+    """(workload, default partition size, draft-verification step?)"""
+    from workloads import CONFIG_NAMES, SPEC_VERIFY_NAME, make_config, make_spec_verify
+    if name == SPEC_VERIFY_NAME:
+        w = make_spec_verify(device=dev) if seed is None else make_spec_verify(seed, dev)
+        return w, SPEC_VERIFY_PS, True
+    index = {v: k for k, v in CONFIG_NAMES.items()}[name]
+    return make_config(index, seed=seed, device=dev), DEFAULT_PS[index], False
 
-    import torch
-    from paged_kv_cache_234_amd import (KVPool, decode_plan_buffer, pa_decode, pa_decode_append,
-                                        pa_decode_plan, pa_decode_cascade,
-                                        pa_decode_multi, pa_decode_splitk_reduce, pa_prefill_chunk,
-                                        pa_selftest)
-    from workloads import make_config, make_spec_verify
 
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    pa_selftest()
-    spec = args.workload == "spec-verify"
-    if spec:
-        w = make_spec_verify(device=dev) if args.seed is None else make_spec_verify(args.seed, dev)
-        ps = SPEC_VERIFY_PS if args.partition_size is None else args.partition_size
-        if ps <= 0:
-            raise SystemExit("the draft-verification step is split-K only (--partition-size > 0)")
-    else:
-        w = make_config(args.config, seed=args.seed, device=dev)
-        ps = DEFAULT_PS[args.config] if args.partition_size is None else args.partition_size
+class LayerStep:
+    """The layer-step the bench times, on device-resident inputs.
 
-    def i32(a):
-        return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev)
+    step(layer, base) enqueues one layer-step on layer copy `layer % R` of
+    the pool: the append of the step's new tokens (inside the decode launch
+    for plain and prefix-shared decode batches), pa_decode_plan when
+    plan_due(layer, base), the decode launch, pa_decode_splitk_reduce and,
+    for the mixed workload, pa_prefill_chunk.  decode_only(layer) enqueues
+    the decode launch alone.  Results land in .out (decode rows, or the
+    draft tokens' rows) and .outp (prefill rows).
 
-    # ---- resident inputs ---------------------------------------------------
-    R = max(2, math.ceil((1 << 30) / w.pool_bytes()))
-    pools = []
-    fill_slots = i32(w.fill_slots)
-    for _ in range(R):
-        p = KVPool(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device=dev,
-                   poison=False, k_scale=w.k_scale, v_scale=w.v_scale)
-        p.append(w.fill_k, w.fill_v, fill_slots)
-        pools.append(p)
-    new_k, new_v = w.new_k.contiguous(), w.new_v.contiguous()
-    new_slots = i32(w.new_slots)
-    if spec:
-        # the query tokens are the rows of the workload's chunks
-        q = w.q_prefill.contiguous()
-        lens, bt = i32(w.chunk_context_lens), i32(w.chunk_block_tables)
-        qsl = i32(w.query_start_loc)
-        max_q = int(np.max(np.diff(w.query_start_loc)))
-        tok_lens = []
-        for c in range(w.num_chunks):
-            n = int(w.query_start_loc[c + 1] - w.query_start_loc[c])
-            tok_lens.extend(int(w.chunk_context_lens[c]) - n + i + 1 for i in range(n))
-        tok_lens = i32(tok_lens)
-        pmax = max(1, -(-int(np.max(w.chunk_context_lens)) // ps))
-    else:
-        q = w.q.contiguous()
-        lens, bt = i32(w.context_lens), i32(w.block_tables)
-        pmax = w.max_partitions(ps)
-    B, hq, d = q.shape
-    part_max = torch.empty((B, hq, pmax), device=dev)
-    part_sum = torch.empty((B, hq, pmax), device=dev)
-    part_out = torch.empty((B, hq, pmax, d), device=dev)
-    out = torch.empty_like(q)
-    # prefix groups: the shared blocks are read once per group (cascade)
-    cascade = bool(w.prefix_groups) and ps > 0 and not args.no_cascade
-    if cascade:
-        g_start, g_seqs, g_plens = [0], [], []
-        for members, nshared in w.prefix_groups:
-            g_seqs.extend(int(b) for b in members)
-            g_start.append(len(g_seqs))
-            g_plens.append(int(nshared) * w.block_size)
-        g_start, g_seqs, g_plens = i32(g_start), i32(g_seqs), i32(g_plens)
-        g_max = max(len(m) for m, _ in w.prefix_groups)
-    has_prefill = w.num_chunks > 0 and not spec
-    # plain and cascade decode steps append each sequence's new token inside
-    # the decode launch (fused: the plain step's pa_decode_append)
-    fuse_append = not (spec or has_prefill or args.no_fuse_append)
-    fused = fuse_append and not cascade
-    if fuse_append:
-        rows = np.zeros(B, np.int64)
-        fslots = np.full(B, -1, np.int32)
-        j = 0
-        for b in range(B):
-            if int(w.context_lens[b]) > 0:
-                rows[b], fslots[b] = w.new_rows[j], w.new_slots[j]
-                j += 1
-        ridx = torch.as_tensor(rows, device=dev)
-        fk, fv, fslots = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous(), i32(fslots)
-    # every decode launch reads its prologue from a plan made once per model
-    # step (the plain decode of the mixed step through pa_decode_append with
-    # no append arrays)
-    planned = not args.no_plan
-    plan = None
-    if planned:
-        plan = decode_plan_buffer(B + (len(w.prefix_groups) if cascade else 0), pools[0].k, d)
+    layer_copies: R (default: enough copies for 1 GiB, at least 2).
+    fill_new: the pools already hold the step's new tokens (the timed steps
+    rewrite them with the same bytes); False leaves those slots to the
+    step's own append, as a test does to check it.
+    poison: unowned pool bytes hold NaN patterns (tests) instead of
+    whatever the allocation held.
+    """
 
-    def make_plan():
-        extra = {}
+    def __init__(self, w, ps, spec, dev, fuse_append=True, planned=True, cascade=True,
+                 layer_copies=None, fill_new=True, poison=False):
+        import torch
+        from paged_kv_cache_234_amd import KVPool, decode_plan_buffer
+        self.w, self.ps, self.spec, self.dev = w, ps, spec, dev
+        i32 = self._i32
+        self.R = layer_copies or max(2, math.ceil((1 << 30) / w.pool_bytes()))
+        rows = np.arange(len(w.fill_slots))
+        if not fill_new:
+            new = set(int(r) for r, s in zip(w.new_rows, w.new_slots) if s >= 0)
+            rows = np.array([r for r in rows if r not in new], dtype=np.int64)
+        ridx = torch.as_tensor(rows, device=w.fill_k.device)
+        fk_all, fv_all = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous()
+        fill_slots = i32(w.fill_slots[rows])
+        self.pools = []
+        for _ in range(self.R):
+            p = KVPool(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device=dev,
+                       poison=poison, k_scale=w.k_scale, v_scale=w.v_scale)
+            p.append(fk_all, fv_all, fill_slots)
+            self.pools.append(p)
+        del fk_all, fv_all
+        self.new_k, self.new_v = w.new_k.contiguous(), w.new_v.contiguous()
+        self.new_slots = i32(w.new_slots)
         if spec:
-            extra = dict(queries=(qsl, max_q))
-        elif cascade:
-            extra = dict(groups=(g_start, g_seqs, g_plens, g_max))
-        pa_decode_plan(plan, bt, lens, w.num_heads, pools[0].k, pools[0].v, partition_size=ps,
-                       max_partitions=pmax, new_slots=fslots if fuse_append else None, **extra)
-    if has_prefill:
-        qp = w.q_prefill.contiguous()
-        outp = torch.empty_like(qp)
-        qsl = i32(w.query_start_loc)
-        maxq = int(np.max(np.diff(w.query_start_loc)))
-        cbt, clens = i32(w.chunk_block_tables), i32(w.chunk_context_lens)
-    torch.cuda.synchronize()
+            # the query tokens are the rows of the workload's chunks
+            self.q = w.q_prefill.contiguous()
+            self.lens, self.bt = i32(w.chunk_context_lens), i32(w.chunk_block_tables)
+            self.qsl = i32(w.query_start_loc)
+            self.max_q = int(np.max(np.diff(w.query_start_loc)))
+            tok_lens = []
+            for c in range(w.num_chunks):
+                n = int(w.query_start_loc[c + 1] - w.query_start_loc[c])
+                tok_lens.extend(int(w.chunk_context_lens[c]) - n + i + 1 for i in range(n))
+            self.tok_lens = i32(tok_lens)
+            self.pmax = max(1, -(-int(np.max(w.chunk_context_lens)) // ps))
+        else:
+            self.q = w.q.contiguous()
+            self.lens, self.bt = i32(w.context_lens), i32(w.block_tables)
+            self.pmax = w.max_partitions(ps) if ps > 0 else 1
+        B, hq, d = self.q.shape
+        self.part_max = torch.empty((B, hq, self.pmax), device=dev)
+        self.part_sum = torch.empty((B, hq, self.pmax), device=dev)
+        self.part_out = torch.empty((B, hq, self.pmax, d), device=dev)
+        self.out = torch.empty_like(self.q)
+        # prefix groups: the shared blocks are read once per group (cascade)
+        self.cascade = bool(w.prefix_groups) and ps > 0 and cascade
+        if self.cascade:
+            g_start, g_seqs, g_plens = [0], [], []
+            for members, nshared in w.prefix_groups:
+                g_seqs.extend(int(b) for b in members)
+                g_start.append(len(g_seqs))
+                g_plens.append(int(nshared) * w.block_size)
+            self.groups = (i32(g_start), i32(g_seqs), i32(g_plens),
+                           max(len(m) for m, _ in w.prefix_groups))
+        self.has_prefill = w.num_chunks > 0 and not spec
+        # plain and cascade decode steps append each sequence's new token
+        # inside the decode launch (fused: the plain step's pa_decode_append)
+        self.fuse_append = not (spec or self.has_prefill) and fuse_append
+        self.fused = self.fuse_append and not self.cascade
+        if self.fuse_append:
+            rows = np.zeros(B, np.int64)
+            fslots = np.full(B, -1, np.int32)
+            j = 0
+            for b in range(B):
+                if int(w.context_lens[b]) > 0:
+                    rows[b], fslots[b] = w.new_rows[j], w.new_slots[j]
+                    j += 1
+            ridx = torch.as_tensor(rows, device=dev)
+            self.fk, self.fv = w.fill_k[ridx].contiguous(), w.fill_v[ridx].contiguous()
+            self.fslots = i32(fslots)
+        # every decode launch reads its prologue from a plan made once per
+        # model step (the plain decode of the mixed step through
+        # pa_decode_append with no append arrays)
+        self.planned = planned
+        self.plan = None
+        if planned:
+            self.plan = decode_plan_buffer(B + (len(w.prefix_groups) if self.cascade else 0),
+                                           self.pools[0].k, d)
+        if self.has_prefill:
+            self.qp = w.q_prefill.contiguous()
+            self.outp = torch.empty_like(self.qp)
+            self.pqsl = i32(w.query_start_loc)
+            self.maxq = int(np.max(np.diff(w.query_start_loc)))
+            self.cbt, self.clens = i32(w.chunk_block_tables), i32(w.chunk_context_lens)
+        self.entry = ("pa_decode_append" if self.fused or (planned and not (spec or self.cascade))
+                      else "pa_decode_multi" if spec else
+                      "pa_decode_cascade" if self.cascade else "pa_decode")
 
-    stream = torch.cuda.current_stream()
+    def _i32(self, a):
+        import torch
+        return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=self.dev)
 
-    def step(layer, ev=None):
-        pool = pools[layer % R]
+    def make_plan(self):
+        from paged_kv_cache_234_amd import pa_decode_plan
+        w = self.w
+        extra = {}
+        if self.spec:
+            extra = dict(queries=(self.qsl, self.max_q))
+        elif self.cascade:
+            extra = dict(groups=self.groups)
+        pa_decode_plan(self.plan, self.bt, self.lens, w.num_heads, self.pools[0].k,
+                       self.pools[0].v, partition_size=self.ps, max_partitions=self.pmax,
+                       new_slots=self.fslots if self.fuse_append else None, **extra)
+
+    def step(self, layer, base, ev=None, stream=None):
+        from paged_kv_cache_234_amd import pa_decode_splitk_reduce, pa_prefill_chunk
+        w, ps = self.w, self.ps
+        pool = self.pools[layer % self.R]
         if ev is not None:
             ev[0].record(stream)
-        if planned and layer % PLAN_LAYERS == 0:
-            make_plan()
-        if not fuse_append:
-            pool.append(new_k, new_v, new_slots)
+        if not self.fuse_append:
+            pool.append(self.new_k, self.new_v, self.new_slots)
         if ev is not None:
             ev[1].record(stream)
-        decode_only(layer)
+        if self.planned and plan_due(layer, base):
+            self.make_plan()
+        self.decode_only(layer)
         if ev is not None:
             ev[2].record(stream)
-        if spec:
-            pa_decode_splitk_reduce(out, part_max, part_sum, part_out, tok_lens, ps)
+        if self.spec:
+            pa_decode_splitk_reduce(self.out, self.part_max, self.part_sum, self.part_out,
+                                    self.tok_lens, ps)
         elif ps > 0:
-            pa_decode_splitk_reduce(out, part_max, part_sum, part_out, lens, ps)
+            pa_decode_splitk_reduce(self.out, self.part_max, self.part_sum, self.part_out,
+                                    self.lens, ps)
         if ev is not None:
             ev[3].record(stream)
-        if has_prefill:
-            pa_prefill_chunk(outp, qp, qsl, maxq, pool.k, pool.v, cbt, clens, w.scale,
-                             pool.k_scale, pool.v_scale)
+        if self.has_prefill:
+            pa_prefill_chunk(self.outp, self.qp, self.pqsl, self.maxq, pool.k, pool.v, self.cbt,
+                             self.clens, w.scale, pool.k_scale, pool.v_scale)
             if ev is not None:
                 ev[4].record(stream)
 
-    def decode_only(layer):
-        pool = pools[layer % R]
-        if fused:
-            pa_decode_append(out if ps == 0 else None, q, fk, fv, fslots, pool.k, pool.v, bt, lens,
-                             w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
-                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
-                             part_out=part_out, plan=plan)
-        elif spec:
-            pa_decode_multi(q, qsl, max_q, pool.k, pool.v, bt, lens, w.scale, ps, pmax, part_max,
-                            part_sum, part_out, pool.k_scale, pool.v_scale, plan=plan)
-        elif cascade:
-            appended = dict(k_new=fk, v_new=fv, new_slots=fslots) if fuse_append else {}
-            pa_decode_cascade(q, pool.k, pool.v, bt, lens, w.scale, g_start, g_seqs, g_plens, g_max,
-                              ps, pmax, part_max, part_sum, part_out, pool.k_scale, pool.v_scale,
-                              plan=plan, **appended)
-        elif planned:
-            pa_decode_append(out if ps == 0 else None, q, None, None, None, pool.k, pool.v, bt,
-                             lens, w.scale, pool.k_scale, pool.v_scale, partition_size=ps,
-                             max_partitions=pmax, part_max=part_max, part_sum=part_sum,
-                             part_out=part_out, plan=plan)
+    def decode_only(self, layer, base=None):
+        from paged_kv_cache_234_amd import (pa_decode, pa_decode_append, pa_decode_cascade,
+                                            pa_decode_multi)
+        w, ps, pmax = self.w, self.ps, self.pmax
+        pool = self.pools[layer % self.R]
+        parts = dict(part_max=self.part_max, part_sum=self.part_sum, part_out=self.part_out)
+        if self.fused:
+            pa_decode_append(self.out if ps == 0 else None, self.q, self.fk, self.fv, self.fslots,
+                             pool.k, pool.v, self.bt, self.lens, w.scale, pool.k_scale,
+                             pool.v_scale, partition_size=ps, max_partitions=pmax, plan=self.plan,
+                             **parts)
+        elif self.spec:
+            pa_decode_multi(self.q, self.qsl, self.max_q, pool.k, pool.v, self.bt, self.lens,
+                            w.scale, ps, pmax, self.part_max, self.part_sum, self.part_out,
+                            pool.k_scale, pool.v_scale, plan=self.plan)
+        elif self.cascade:
+            g_start, g_seqs, g_plens, g_max = self.groups
+            appended = (dict(k_new=self.fk, v_new=self.fv, new_slots=self.fslots)
+                        if self.fuse_append else {})
+            pa_decode_cascade(self.q, pool.k, pool.v, self.bt, self.lens, w.scale, g_start,
+                              g_seqs, g_plens, g_max, ps, pmax, self.part_max, self.part_sum,
+                              self.part_out, pool.k_scale, pool.v_scale, plan=self.plan,
+                              **appended)
+        elif self.planned:
+            pa_decode_append(self.out if ps == 0 else None, self.q, None, None, None, pool.k,
+                             pool.v, self.bt, self.lens, w.scale, pool.k_scale, pool.v_scale,
+                             partition_size=ps, max_partitions=pmax, plan=self.plan, **parts)
         elif ps > 0:
-            pa_decode(None, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale,
-                      partition_size=ps, max_partitions=pmax, part_max=part_max,
-                      part_sum=part_sum, part_out=part_out)
+            pa_decode(None, self.q, pool.k, pool.v, self.bt, self.lens, w.scale, pool.k_scale,
+                      pool.v_scale, partition_size=ps, max_partitions=pmax, **parts)
         else:
-            pa_decode(out, q, pool.k, pool.v, bt, lens, w.scale, pool.k_scale, pool.v_scale)
+            pa_decode(self.out, self.q, pool.k, pool.v, self.bt, self.lens, w.scale,
+                      pool.k_scale, pool.v_scale)
 
+
+def run_workload(name, args, dev):
+    """Time one workload; returns its record (all figures but the CPU legs)
+    and the workload itself."""
+    import torch
+
+    w, ps, spec = make_workload(name, args.seed, dev)
+    if args.partition_size is not None:
+        ps = args.partition_size
+    if spec and ps <= 0:
+        raise SystemExit("the draft-verification step is split-K only (--partition-size > 0)")
+    ls = LayerStep(w, ps, spec, dev, fuse_append=not args.no_fuse_append,
+                   planned=not args.no_plan, cascade=not args.no_cascade)
+    planned, fuse_append, fused, has_prefill = ls.planned, ls.fuse_append, ls.fused, ls.has_prefill
+    cascade = ls.cascade
+    step, decode_only, make_plan = ls.step, ls.decode_only, ls.make_plan
+    pmax, R = ls.pmax, ls.R
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    warm = max(args.warmup, 1)
     if planned:
         make_plan()
-    for i in range(max(args.warmup, 1)):
-        step(i)
+    for i in range(warm):
+        step(i, 0)
         decode_only(i)
     torch.cuda.synchronize()
 
     # The engines on the pages replay their decode step as a captured graph
     # covering every layer; here one graph holds the K timed layer-steps (each
     # on the next layer copy), another the warm-up steps, a third the K
-    # decode kernels alone.
+    # decode kernels alone (reading the plan the steps before made).
     def steps_of(fn, first, count):
         for i in range(count):
-            fn(first + i)
+            fn(first + i, first)
 
     def captured(fn, first, count):
         g = torch.cuda.CUDAGraph()
@@ -259,14 +358,14 @@ def main():
         return g
 
     if not args.eager:
-        g_warm = captured(step, 0, max(args.warmup, 1))
+        g_warm = captured(step, 0, warm)
         g_steps = captured(step, args.warmup, args.steps)
         g_decode = captured(decode_only, args.warmup, args.steps)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         g_warm.replay()
     else:
-        steps_of(step, 0, args.warmup)
+        steps_of(step, 0, warm)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ------------------------------------
@@ -297,16 +396,27 @@ def main():
     # ---- per-kernel durations, eager, HIP events around each launch ---------
     nev = 5 if has_prefill else 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    first = args.warmup + args.steps
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
+        step(first + i, first, evs[i], stream)
     torch.cuda.synchronize()
-    names = (["(append fused)" + (", plan / %d layers" % PLAN_LAYERS if planned else ""),
-              "decode_append" if fused else "decode"] if fuse_append else
-             ["kv_append", "decode"]) + \
-        ["splitk_reduce", "prefill_chunk"]
+    names = ["append" if fuse_append else "kv_append",
+             ("plan / %d layers + " % PLAN_LAYERS if planned else "") +
+             ("decode_append" if fused else "decode"), "splitk_reduce", "prefill_chunk"]
     names = names[:nev - 1]
     kern_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                for j, n in enumerate(names)}
+    if fuse_append:
+        del kern_ms["append"]                     # inside the decode launch
+    plan_us = None
+    if planned:
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(args.steps):
+            make_plan()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        plan_us = p0.elapsed_time(p1) * 1e3 / args.steps
 
     # ---- accounting -----------------------------------------------------------
     kv_logical = w.prefill_kv_bytes() if spec else w.decode_kv_bytes_logical()
@@ -315,79 +425,140 @@ def main():
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_unique / (decode_ms * 1e-3) / 1e9
 
-    # achievable copy bandwidth, same process (context for the peak)
-    nbytes = 1 << 30
-    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
-    result_entry = ("pa_decode_append" if fused or (planned and not (spec or cascade)) else
-                    "pa_decode_multi" if spec else "pa_decode_cascade" if cascade else "pa_decode")
-    result = {
-        "metric": METRIC,
-        "value": round(gbps, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    entry = ls.entry
+    rec = {
+        "workload": w.name,
+        "gate_70pct_hbm": w.name in GATE,
+        "us_per_layer_step": round(ms_per_step * 1e3, 3),
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "kv_GBps": round(gbps, 2),
+        "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),
+        "kv_bytes_logical": kv_logical,
+        "kv_bytes_unique": kv_unique,
+        "decode_kernel_us": round(decode_ms * 1e3, 3),
+        "eager_event_us": {k: round(v * 1e3, 3) for k, v in kern_ms.items()},
+        "plan_us": None if plan_us is None else round(plan_us, 3),
         "dtype": w.cache_dtype if w.cache_dtype != "fp8" else "fp8-e4m3 KV, bf16 Q",
-        "data": "synthetic (seeded; no dataset, no weights)",
         "config": {
             "workload": w.name, "seed": w.seed, "batch": w.num_chunks if spec else w.batch,
             "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size,
             "context_tokens": int((w.chunk_context_lens if spec else w.context_lens).sum()),
             "new_tokens": int(len(w.new_slots)),
-            "prefill_chunks": w.num_chunks, "partition_size": ps, "max_partitions": pmax,
-            "pool_blocks": w.num_blocks, "layer_copies": R,
-            "decode_entry": result_entry,
-            "plan": ("pa_decode_plan once per %d layer-steps" % PLAN_LAYERS) if planned else None,
+            "prefill_chunks": 0 if spec else w.num_chunks, "partition_size": ps,
+            "max_partitions": pmax, "pool_blocks": w.num_blocks, "layer_copies": R,
+            "decode_entry": entry,
+            "plan": ("pa_decode_plan once per %d layer-steps, inside the timed graph"
+                     % PLAN_LAYERS) if planned else None,
             "step_entries": ("pa_decode_cascade (append fused) + pa_decode_splitk_reduce"
                              if fuse_append and cascade else
                              "pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (
-                                 result_entry,
-                                 " + pa_decode_splitk_reduce" if ps > 0 else "",
+                                 entry, " + pa_decode_splitk_reduce" if ps > 0 else "",
                                  " + pa_prefill_chunk" if has_prefill else "")),
         },
-        "us_per_layer_step": round(ms_per_step * 1e3, 3),
-        "pct_hbm_peak": round(100.0 * (kv_unique / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBPS, 2),
-        "kv_bytes_logical": kv_logical,
-        "kv_bytes_unique": kv_unique,
         "launch": "eager" if args.eager else "one HIP graph holding the K layer-steps",
-        "decode_kernel_us": round(decode_ms * 1e3, 3),
-        "eager_event_us": {k: round(v * 1e3, 3) for k, v in kern_ms.items()},
-        "copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": result_entry,
+            "kernel": entry,
             "duration_us": round(decode_ms * 1e3, 3),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w.name, ps, result_entry),
+            "traffic": measured_traffic(w.name, ps, entry),
         },
     }
     if has_prefill:
         pf_ms = kern_ms["prefill_chunk"]
-        result["prefill_tflops"] = round(w.prefill_flops() / (pf_ms * 1e-3) / 1e12, 2)
+        rec["prefill_tflops"] = round(w.prefill_flops() / (pf_ms * 1e-3) / 1e12, 2)
+        rec["prefill_mfma_frac_bf16"] = round(rec["prefill_tflops"] / 2500.0, 4)
+    del ls
+    if not args.eager:
+        del g_warm, g_steps, g_decode
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, w
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, ms_per_step, kv_logical)
+
+def copy_bandwidth(dev):
+    """Achievable copy bandwidth in this process (context for the peak)."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * nbytes * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
+def main(argv=None):
+    args = parse(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the paged-attention path here is built and timed on "
+              "a single MI355X (no sharding, no collectives); --gpus %d is not supported"
+              % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_234_amd import pa_selftest
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    names = workload_names() if args.workload == "all" else [args.workload]
+    headline = HEADLINE if HEADLINE in names else names[0]
+    recs = {}
+    for name in names:
+        pa_selftest()             # (also marks where each workload starts in a kernel trace)
+        print("bench: %s" % name, file=sys.stderr, flush=True)
+        rec, w = run_workload(name, args, dev)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"], rec["cpu_baseline_1thread"] = cpu_baselines(
+                w, args.cpu_seconds, args.cpu_seconds_1t, rec["ms_per_step"],
+                rec["kv_bytes_logical"])
+        del w
+        recs[name] = rec
+    copy_gbps = copy_bandwidth(dev)
+
+    h = recs[headline]
+    result = {
+        "metric": METRIC,
+        "value": h["kv_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": h["dtype"],
+        "data": "synthetic (seeded; no dataset, no weights)",
+        "config": h["config"],
+        "us_per_layer_step": h["us_per_layer_step"],
+        "pct_hbm_peak": h["pct_hbm_peak"],
+        "kv_bytes_logical": h["kv_bytes_logical"],
+        "kv_bytes_unique": h["kv_bytes_unique"],
+        "launch": h["launch"],
+        "decode_kernel_us": h["decode_kernel_us"],
+        "copy_GBps": round(copy_gbps, 1),
+        "roofline": h["roofline"],
+    }
+    if "cpu_baseline" in h:
+        result["cpu_baseline"] = h["cpu_baseline"]
+        result["cpu_baseline_1thread"] = h["cpu_baseline_1thread"]
+    if len(recs) > 1:
+        result["headline"] = ("the long-context batch: the largest workload one GPU holds; "
+                              "'configs' has every workload")
+        result["configs"] = recs
     print(json.dumps(result), flush=True)
 
 
@@ -425,17 +596,25 @@ def measured_traffic(workload, ps, entry):
     return None
 
 
-def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes):
+def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes, one_thread=False):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     decode sequences (or, for a workload of chunks only, its chunks); scaled
-    to the metric's unit (KV GB/s)."""
+    to the metric's unit (KV GB/s).  one_thread: BLAS limited to one thread
+    (the rest of the oracle is single-threaded NumPy either way)."""
+    if one_thread:
+        return cpu_baselines(w, 0.0, budget_s, gpu_ms, gpu_bytes, all_cores=False)[1]
+    return cpu_baselines(w, budget_s, None, gpu_ms, gpu_bytes)[0]
+
+
+def cpu_baselines(w, budget_s, budget_1t, gpu_ms, gpu_bytes, all_cores=True):
+    """(all-core record, one-thread record or None).  The all-core leg fills
+    the oracle's pool sequence by sequence as it goes (untimed) and times
+    each sequence; the one-thread leg times the sequences the pool already
+    holds (at least one) with BLAS limited to one thread."""
     from oracle import paged_attention as opa
     import torch
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
 
     def raw(t):
         t = t.detach().cpu().contiguous()
@@ -445,59 +624,77 @@ def cpu_baseline(w, budget_s, gpu_ms, gpu_bytes):
     n_units = w.num_chunks if chunks_only else w.batch
     lens_of = w.chunk_context_lens if chunks_only else w.context_lens
     tables_of = w.chunk_block_tables if chunks_only else w.block_tables
-    rng = np.random.default_rng(0)
-    order = rng.permutation(n_units)
+    order = np.random.default_rng(0).permutation(n_units)
     st = opa.STORAGE_DTYPES[w.cache_dtype]
     shape_k, shape_v = opa.pool_shapes(w.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
                                        w.block_size)
-    kp = np.zeros(shape_k, st)
-    vp = np.zeros(shape_v, st)
+    pool = [np.zeros(shape_k, st), np.zeros(shape_v, st)]
     qh = raw(w.q_prefill if chunks_only else w.q)
-    # The first pass fills the oracle's pool sequence by sequence (untimed)
-    # and times each sequence; when the whole workload takes less than the
-    # budget, further passes over the same pool repeat the timed part.
-    done, tokens, elapsed, passes = [], 0, 0.0, 0
-    while elapsed < budget_s or not done:          # at least one sequence
-        for b in order:
-            if passes == 0:
-                n = -(-int(lens_of[b]) // w.block_size)
-                blocks = tables_of[b, :n].astype(np.int64)
-                sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
-                idx = torch.as_tensor(sel, device=w.fill_k.device)
-                kp, vp = opa.oracle_append(kp, vp, raw(w.fill_k[idx]), raw(w.fill_v[idx]),
-                                           w.fill_slots[sel], w.in_dtype, w.cache_dtype,
-                                           w.k_scale, w.v_scale, w.block_size)
-            elif int(b) not in done_set:
-                continue
-            t = time.perf_counter()
-            if chunks_only:
-                opa.oracle_prefill(qh, w.q_dtype, w.query_start_loc, kp, vp, w.cache_dtype,
-                                   w.chunk_block_tables, w.chunk_context_lens, w.scale, w.k_scale,
-                                   w.v_scale, w.block_size, chunks=[int(b)])
-            else:
-                opa.oracle_decode(qh, w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
-                                  w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size,
-                                  seqs=[int(b)])
-            elapsed += time.perf_counter() - t
-            if passes == 0:
-                done.append(int(b))
-            tokens += int(lens_of[b])
-            if elapsed >= budget_s:
-                break
-        passes += 1
-        done_set = set(done)
-    kv = tokens * w.kv_bytes_per_token()
+    filled = []
+
+    def fill(b):
+        n = -(-int(lens_of[b]) // w.block_size)
+        blocks = tables_of[b, :n].astype(np.int64)
+        sel = np.flatnonzero(np.isin(w.fill_slots // w.block_size, blocks))
+        idx = torch.as_tensor(sel, device=w.fill_k.device)
+        pool[0], pool[1] = opa.oracle_append(pool[0], pool[1], raw(w.fill_k[idx]),
+                                             raw(w.fill_v[idx]), w.fill_slots[sel], w.in_dtype,
+                                             w.cache_dtype, w.k_scale, w.v_scale, w.block_size)
+        filled.append(int(b))
+
+    def timed(b):
+        t = time.perf_counter()
+        if chunks_only:
+            opa.oracle_prefill(qh, w.q_dtype, w.query_start_loc, pool[0], pool[1],
+                               w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens,
+                               w.scale, w.k_scale, w.v_scale, w.block_size, chunks=[int(b)])
+        else:
+            opa.oracle_decode(qh, w.q_dtype, pool[0], pool[1], w.cache_dtype, w.block_tables,
+                              w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size,
+                              seqs=[int(b)])
+        return time.perf_counter() - t
+
+    def leg(budget, grow, nthreads):
+        """Passes over the workload until the budget is spent (at least one
+        sequence); grow: the first pass adds sequences to the pool."""
+        used, tokens, elapsed, passes = set(), 0, 0.0, 0
+        while elapsed < budget or not used:
+            seq = order if (grow and passes == 0) else [b for b in order if int(b) in filled]
+            for b in seq:
+                if int(b) not in filled:
+                    fill(b)
+                elapsed += timed(b)
+                used.add(int(b))
+                tokens += int(lens_of[b])
+                if elapsed >= budget:
+                    break
+            passes += 1
+        kv = tokens * w.kv_bytes_per_token()
+        return _baseline_record(w, kv, elapsed, nthreads, used, n_units, passes, tokens,
+                                chunks_only, gpu_ms, gpu_bytes)
+
+    rec_all = leg(budget_s, True, threads) if all_cores else None
+    rec_1t = None
+    if budget_1t is not None:
+        if not filled:
+            fill(order[0])
+        with threadpool_limits(limits=1):
+            rec_1t = leg(budget_1t, False, 1)
+    return rec_all, rec_1t
+
+
+def _baseline_record(w, kv, elapsed, threads, done, n_units, passes, tokens, chunks_only,
+                     gpu_ms, gpu_bytes):
     return {
         "value": round(kv / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": "fp64 oracle %s of %d of %d %s, %d pass(es) (%d context tokens, %.1f s), "
-                  "host affinity %d cores" % ("causal chunks" if chunks_only else "decode",
-                                              len(done), n_units,
-                                              "sequences' query tokens" if chunks_only else
-                                              "sequences", passes, tokens, elapsed,
-                                              len(os.sched_getaffinity(0))),
+                  "host affinity %d cores, BLAS threads %d" % (
+                      "causal chunks" if chunks_only else "decode", len(done), n_units,
+                      "sequences' query tokens" if chunks_only else "sequences", passes, tokens,
+                      elapsed, len(os.sched_getaffinity(0)), threads),
         "seconds": round(elapsed, 3),
         "gpu_over_cpu": round((gpu_bytes / (gpu_ms * 1e-3)) / (kv / elapsed), 1)
         if elapsed > 0 else None,

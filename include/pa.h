@@ -172,7 +172,10 @@ pa_status_t pa_decode(void* out, const void* q, pa_dtype_t q_dtype,
  *                  cache dtype, partition_size and max_partitions on this
  *                  device: the launch then skips its prologue (see
  *                  pa_decode_plan).  A plan whose header does not match
- *                  these arguments makes the launch do nothing.
+ *                  these arguments makes the launch append and compute
+ *                  nothing and write NaN to every element of `out` (single
+ *                  pass) or of the three partial buffers (split-K), so the
+ *                  mistake shows in the results instead of passing silently.
  *   plan_bytes     the plan buffer's size; less than pa_decode_plan_bytes
  *                  for this batch returns PA_ERR_ARG
  * Other arguments, outputs, layouts and errors as pa_decode; the pools are

@@ -59,3 +59,30 @@ def test_traffic_lookup_refuses_other_partitions_and_entries():
 def test_bench_defaults_match_the_summaries():
     assert bench.DEFAULT_PS[5] == 1024 and bench.SPEC_VERIFY_PS == 512
     assert os.path.isdir(os.path.join(bench.ROOT, "profiles"))
+
+
+def test_one_thread_leg_reuses_the_pool_and_limits_blas():
+    w = make_config(1, device="cpu")
+    rec_all, rec_1t = bench.cpu_baselines(w, 0.2, 0.1, 0.01, 441344)
+    assert rec_all["cores"] >= 1 and rec_1t["cores"] == 1
+    assert "BLAS threads 1" in rec_1t["sample"]
+    assert rec_1t["seconds"] >= 0.1 and rec_1t["value"] > 0
+
+
+@pytest.mark.parametrize("k", [1, 5, 20, 31, 32, 33, 50, 64, 100])
+@pytest.mark.parametrize("base", [0, 5, 10, 37])
+def test_every_timed_region_holds_its_share_of_plans(k, base):
+    """A captured region of K layer-steps starting anywhere makes
+    ceil(K / PLAN_LAYERS) plans, the first at its first step."""
+    due = [bench.plan_due(base + i, base) for i in range(k)]
+    assert due[0] and sum(due) == -(-k // bench.PLAN_LAYERS)
+
+
+def test_default_run_times_every_workload_with_the_long_context_headline():
+    args = bench.parse([])
+    assert args.workload == "all" and args.gpus == 1
+    names = bench.workload_names()
+    assert len(names) == 6 and bench.HEADLINE in names
+    assert set(bench.GATE) <= set(names)
+    assert args.cpu_seconds * len(names) <= 30          # a bounded CPU sample
+    assert bench.parse(["--config", "4"]).workload == bench.HEADLINE

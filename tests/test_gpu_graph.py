@@ -1,7 +1,9 @@
 """A captured layer-step (append + split-K decode + reduce + prefill chunk)
 replays to exactly the eager result, replay after replay, with eager work and
-synchronisations in between (the engines on the pages capture each decode
-step in a graph: InferX milestone M6, llm-infer "What It Does", RustInfer)."""
+synchronisations in between, and every replay matches the fp64 oracle (the
+engines on the pages capture each decode step in a graph: InferX milestone
+M6, llm-infer "What It Does", RustInfer).  The full-size step bench.py
+captures is covered in test_gpu_full_size.py."""
 
 import numpy as np
 import pytest
@@ -9,10 +11,22 @@ import torch
 
 from paged_kv_cache_234_amd import (pa_decode, pa_decode_splitk_reduce, pa_kv_append,
                                     pa_prefill_chunk)
-from tests.gpu_helpers import gpu_pool, i32
+from oracle import paged_attention as opa
+from tests.gpu_helpers import TOL, as_f64, gpu_pool, host, i32, max_abs_err, oracle_pool
 from workloads import build_workload
 
 pytestmark = pytest.mark.gpu
+
+
+def _oracle(w):
+    """Decode rows and prefill rows of the workload, fp64 oracle."""
+    kp, vp = oracle_pool(w)
+    dec = opa.oracle_decode(host(w.q), w.q_dtype, kp, vp, w.cache_dtype, w.block_tables,
+                            w.context_lens, w.scale, w.k_scale, w.v_scale, w.block_size)
+    pre = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
+                             w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens, w.scale,
+                             w.k_scale, w.v_scale, w.block_size)
+    return dec, pre
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
@@ -48,6 +62,7 @@ def test_graph_replays_equal_eager(cache):
     torch.cuda.synchronize()
     ref, refp = out.clone(), outp.clone()
     kref, vref = pool.k.clone(), pool.v.clone()
+    dec, pre = _oracle(w)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -61,6 +76,8 @@ def test_graph_replays_equal_eager(cache):
         torch.cuda.synchronize()
         assert torch.equal(out, ref), "decode output differs on replay %d" % rep
         assert torch.equal(outp, refp), "prefill output differs on replay %d" % rep
+        assert max_abs_err(as_f64(out), dec) <= TOL[cache]
+        assert max_abs_err(as_f64(outp), pre) <= TOL[cache]
         # bytes, not values: unowned slots hold NaN patterns
         assert torch.equal(pool.k.view(torch.uint8), kref.view(torch.uint8))
         assert torch.equal(pool.v.view(torch.uint8), vref.view(torch.uint8))
@@ -127,6 +144,10 @@ def test_two_stream_graph_replays_equal_serial_eager(cache):
     torch.cuda.synchronize()
     ref, refp = out.clone(), outp.clone()
     kref, vref = pool.k.clone(), pool.v.clone()
+
+    dec, pre = _oracle(w)
+    assert max_abs_err(as_f64(ref), dec) <= TOL[cache]
+    assert max_abs_err(as_f64(refp), pre) <= TOL[cache]
 
     def check(what):
         assert torch.equal(out, ref), "decode output differs: %s" % what
