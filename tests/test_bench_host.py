@@ -36,6 +36,7 @@ def test_cpu_baseline_stops_inside_a_pass_when_the_budget_is_spent():
 
 
 @pytest.mark.parametrize("workload,ps,entry", [
+    ("tiny-fp32-decode", 16, "pa_decode_append"),
     ("qwen2.5-3b-bf16-decode-b64", 256, "pa_decode_append"),
     ("llama3-8b-bf16-decode-prefix-shared-b256", 256, "pa_decode_cascade"),
     ("long-context-bf16-splitk-b8", 512, "pa_decode_append"),
@@ -57,7 +58,7 @@ def test_traffic_lookup_refuses_other_partitions_and_entries():
 
 
 def test_bench_defaults_match_the_summaries():
-    assert bench.DEFAULT_PS[5] == 1024 and bench.SPEC_VERIFY_PS == 512
+    assert bench.DEFAULT_PS[5] == 1024 and bench.SPEC_VERIFY_PS == 512 and bench.DEFAULT_PS[1] == 16
     assert os.path.isdir(os.path.join(bench.ROOT, "profiles"))
 
 
