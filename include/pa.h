@@ -96,7 +96,8 @@ typedef enum {
     PA_OK = 0,
     PA_ERR_ARG = 1,          /* NULL pointer, negative or inconsistent size */
     PA_ERR_UNSUPPORTED = 2,  /* dtype / head_dim / block_size / G not built */
-    PA_ERR_LAUNCH = 3        /* the HIP runtime refused a launch */
+    PA_ERR_LAUNCH = 3,       /* the HIP runtime refused a launch */
+    PA_ERR_TOO_LARGE = 4     /* pa_decode_noalloc: partials beyond its static scratch */
 } pa_status_t;
 
 /* The decode entry point a launch plan is made for (pa_decode_plan). */
@@ -352,6 +353,38 @@ pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_dtype,
                              const int32_t* context_lens,
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t block_size, float scale, hipStream_t stream);
+
+/*
+ * Split-K decode that allocates nothing, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid it) and so cannot pass pa_decode's partial buffers.  It is
+ * pa_decode with partition_size > 0 followed by pa_decode_splitk_reduce,
+ * with the partials in a fixed scratch array that the library holds in each
+ * GPU's memory until the process ends; `out` gets the same bits those two
+ * calls give.
+ *   out            [batch][num_heads][head_dim] of q_dtype
+ *   partition_size > 0, a multiple of 16 (PA_ERR_ARG otherwise)
+ *   other arguments as pa_decode
+ * Requires the partials to fit the scratch: 256-aligned part_max and part_sum
+ * of batch * num_heads * max_partitions floats each, then part_out of
+ * head_dim times that, within pa_decode_noalloc_max_bytes() = 64 MiB (e.g.
+ * batch 8, 32 heads, head_dim 128, 256 partitions: 32.5 MiB).  Larger sizes
+ * return PA_ERR_TOO_LARGE before anything is launched.  Calls on one GPU
+ * share its scratch, so calls that overlap on one GPU (other streams, other
+ * threads) race; calls ordered on one stream do not.
+ */
+pa_status_t pa_decode_noalloc(void* out, const void* q, pa_dtype_t q_dtype,
+                              const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, float scale,
+                              int32_t partition_size, int32_t max_partitions,
+                              hipStream_t stream);
+
+/* The size of pa_decode_noalloc's scratch on each GPU, in bytes. */
+size_t pa_decode_noalloc_max_bytes(void);
 
 /*
  * Name of a status code: a static string, never NULL.  Every call above

@@ -16,13 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_FP8_E4M3 = 0, 1, 2
-PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
+PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 BLOCK_SIZE = 16
 
 EXPORTED = (
     "pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade", "pa_decode_multi",
     "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_decode_plan", "pa_decode_plan_bytes",
-    "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest",
+    "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest", "pa_decode_noalloc",
+    "pa_decode_noalloc_max_bytes",
 )
 
 _lib = None
@@ -69,9 +70,13 @@ def load(path=LIB_PATH):
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_selftest.argtypes = []
+    lib.pa_decode_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32,
+                                      i32, i32, f32, i32, i32, st]
+    lib.pa_decode_noalloc_max_bytes.argtypes = []
+    lib.pa_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     for fn in ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade",
                "pa_decode_multi", "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_decode_plan",
-               "pa_selftest"):
+               "pa_selftest", "pa_decode_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -238,6 +243,29 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_sca
                           int(partition_size), int(max_partitions), _ptr(part_max),
                           _ptr(part_sum), _ptr(part_out), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      partition_size, max_partitions, k_scale=None, v_scale=None, stream=None):
+    """Split-K decode + reduce into out [B, Hq, D] with the partials in the
+    library's static per-GPU scratch (no device memory from the caller)."""
+    nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
+    B, hq = q.shape[0], q.shape[1]
+    if q.shape[2] != d or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("inconsistent decode shapes")
+    if out is None or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = load().pa_decode_noalloc(_ptr(out), _ptr(q), _dt(q), _ptr(k_cache), _ptr(v_cache),
+                                  _dt(k_cache), _ptr(k_scale), _ptr(v_scale),
+                                  _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                  _i32(context_lens, "context_lens"), B, hq, hkv, d, bs,
+                                  float(scale), int(partition_size), int(max_partitions),
+                                  _stream(stream))
+    _check("pa_decode_noalloc", st)
+
+
+def pa_decode_noalloc_max_bytes():
+    return int(load().pa_decode_noalloc_max_bytes())
 
 
 def pa_decode_append(out, q, k_new, v_new, new_slots, k_cache, v_cache, block_tables,

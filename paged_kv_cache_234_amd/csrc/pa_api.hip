@@ -30,6 +30,7 @@ extern "C" const char* pa_status_string(pa_status_t s) {
         case PA_ERR_ARG: return "PA_ERR_ARG: null pointer or invalid size";
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype/head_dim/block_size/GQA combination not built";
         case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+        case PA_ERR_TOO_LARGE: return "PA_ERR_TOO_LARGE: the partials exceed pa_decode_noalloc's static scratch";
     }
     return "PA_ERR_UNKNOWN";
 }

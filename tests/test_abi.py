@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(4):
+    for s in range(5):
         assert _lib.status_string(s).startswith("PA_")
     assert _lib.status_string(99) == "PA_ERR_UNKNOWN"
 
@@ -179,3 +179,28 @@ def test_decode_plan_validation():
     assert lib.pa_decode_plan_bytes(64, 1, 64) > lib.pa_decode_plan_bytes(64, 1, 128)
     assert lib.pa_decode_plan_bytes(-1, 1, 128) == 0
     assert lib.pa_decode_plan_bytes(64, 1, 96) == 0
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, q_dt=1, k=FAKE, v=FAKE, c_dt=1, ks=None, vs=None, bt=FAKE, W=4,
+             lens=FAKE, B=2, hq=8, hkv=2, d=128, bs=16, scale=0.1, ps=64, pmax=4)
+    a.update(kw)
+    return lib.pa_decode_noalloc(a["out"], a["q"], a["q_dt"], a["k"], a["v"], a["c_dt"], a["ks"],
+                                 a["vs"], a["bt"], a["W"], a["lens"], a["B"], a["hq"], a["hkv"],
+                                 a["d"], a["bs"], a["scale"], a["ps"], a["pmax"], None)
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_partials_before_any_device_call():
+    """Every host check runs before the device is touched: partials beyond
+    the static scratch (64 MiB) are PA_ERR_TOO_LARGE, split-K is required."""
+    lib = _lib.load()
+    assert lib.pa_decode_noalloc_max_bytes() == 64 << 20
+    assert _noalloc(lib, ps=0) == _lib.PA_ERR_ARG
+    assert _noalloc(lib, ps=24) == _lib.PA_ERR_ARG
+    assert _noalloc(lib, pmax=0) == _lib.PA_ERR_ARG
+    assert _noalloc(lib, out=None) == _lib.PA_ERR_ARG
+    assert _noalloc(lib, d=96) == _lib.PA_ERR_UNSUPPORTED
+    assert _noalloc(lib, B=0) == _lib.PA_OK
+    # 8 x 32 heads x 512 partitions x 130 floats = 65 MiB of partials > 64 MiB
+    assert _noalloc(lib, B=8, hq=32, hkv=8, pmax=512) == _lib.PA_ERR_TOO_LARGE
+    assert _noalloc(lib, B=4096, hq=16, pmax=64) == _lib.PA_ERR_TOO_LARGE
