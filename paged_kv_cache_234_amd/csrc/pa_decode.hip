@@ -932,10 +932,70 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < TB; ++j) phys[j] = load_invariant(bt + min(lb + j, last));
         };
+        // The plan's list of the tokens this wavefront appends (D / 8 lanes
+        // carry one token, so a register set holds 512 / D): their rows are
+        // loaded before anything else.  The stores must precede the loads of
+        // the tile holding the token (the last tile of a listed (row, KV
+        // head)), which then reads it back.  The plain kernel issues them just
+        // before that tile's loads -- usually tiles later, when the rows have
+        // long arrived, so the stream never waits for them.  The wide kernels
+        // have no registers to hold the rows that long: they store as soon as
+        // the rows arrive, after the first tile's loads (before them when the
+        // first tile holds a token).
+        constexpr bool kDeferStores = NC == 1;
+        constexpr int CPT = D / 8, TPP = kWave / CPT;
+        constexpr int NP = (kPlanMaxAppends + TPP - 1) / TPP;
+        TokenChunk<KIND> tok[NP];
+        int t_rh[NP], t_slot[NP];
+        const bool listed = listed_appends && plan_apps > 0;
+        bool stored = !listed;
+        if (listed) {
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int ti = j * TPP + lane / CPT;
+                int rh = plan_app_rh[0], slot = -1;
+#pragma unroll
+                for (int i = 0; i < kPlanMaxAppends; ++i)
+                    if (i == ti && i < plan_apps) {
+                        rh = plan_app_rh[i];
+                        slot = plan_app_slot[i];
+                    }
+                t_rh[j] = rh;
+                t_slot[j] = slot;
+                const long row = (long)rh * D * IB;
+                tok[j] = load_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
+                                                   static_cast<const char*>(a.v_new) + row,
+                                                   lane % CPT);
+            }
+        }
+        auto store_all = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                if (j * TPP >= plan_apps) break;
+                const int h = t_rh[j] % Hkv, slot = t_slot[j];
+                if (slot >= 0) {
+                    float ksc, vsc;
+                    scales(h, ksc, vsc);
+                    store_token_chunk<KIND, D>(tok[j], a.k_cache_w, a.v_cache_w, slot / kBlock,
+                                               slot % kBlock, h, Hkv, lane % CPT, ksc, vsc);
+                }
+            }
+            stored = true;
+        };
+        // the tile under cursor c holds a listed token not stored yet
+        auto holds_token = [&](const Cursor& c) __attribute__((always_inline)) {
+            if (stored || c.p + 1 != c.n || c.jj + 1 != c.nti) return false;
+            bool hit = false;
+#pragma unroll
+            for (int i = 0; i < kPlanMaxAppends; ++i)
+                hit |= i < plan_apps && plan_app_rh[i] == c.r * Hkv + c.h;
+            return hit;
+        };
         // load the tile under the load cursor and move the cursor on; the
         // next tile's block ids and (entering an item) Q go out first
         // FIRST: the launch's first load, whose successor's block ids a plan holds
         auto issue = [&](typename Ops::Regs& r, auto first) {
+            const bool store_now = kDeferStores && holds_token(lc);
             const long hoff = (long)lc.h * head_stride;
             int ph[TB];
 #pragma unroll
@@ -959,6 +1019,7 @@ void decode_kernel(DecodeArgs a) {
                     }
                 }
             }
+            if (store_now) store_all();
             Ops::load(r, a.k_cache + hoff, a.v_cache + hoff, blk_stride, ph, lane);
         };
         int ncomputed = 0;
@@ -1013,57 +1074,9 @@ void decode_kernel(DecodeArgs a) {
         }
         typename Ops::Regs ra, rb;
         // tile i is computed while tile i + 1 is in flight
-        if (listed_appends && plan_apps > 0) {
-            // The plan's list: every row's loads go out first, then the first
-            // tile's K/V loads unless that tile is the last of a listed (row,
-            // KV head) -- the one holding its new token -- then the stores.
-            // D / 8 lanes carry one token, so a register set holds 512 / D.
-            constexpr int CPT = D / 8, TPP = kWave / CPT;
-            constexpr int NP = (kPlanMaxAppends + TPP - 1) / TPP;
-            TokenChunk<KIND> tok[NP];
-            int t_rh[NP], t_slot[NP];
-#pragma unroll
-            for (int j = 0; j < NP; ++j) {
-                const int ti = j * TPP + lane / CPT;
-                int rh = plan_app_rh[0], slot = -1;
-#pragma unroll
-                for (int i = 0; i < kPlanMaxAppends; ++i)
-                    if (i == ti && i < plan_apps) {
-                        rh = plan_app_rh[i];
-                        slot = plan_app_slot[i];
-                    }
-                t_rh[j] = rh;
-                t_slot[j] = slot;
-                const long row = (long)rh * D * IB;
-                tok[j] = load_token_chunk<KIND, D>(static_cast<const char*>(a.k_new) + row,
-                                                   static_cast<const char*>(a.v_new) + row,
-                                                   lane % CPT);
-            }
-            auto store_all = [&]() {
-#pragma unroll
-                for (int j = 0; j < NP; ++j) {
-                    if (j * TPP >= plan_apps) break;
-                    const int h = t_rh[j] % Hkv, slot = t_slot[j];
-                    if (slot >= 0) {
-                        float ksc, vsc;
-                        scales(h, ksc, vsc);
-                        store_token_chunk<KIND, D>(tok[j], a.k_cache_w, a.v_cache_w, slot / kBlock,
-                                                   slot % kBlock, h, Hkv, lane % CPT, ksc, vsc);
-                    }
-                }
-            };
-            bool first_holds = false;
-            if (cc.p + 1 == cc.n && cc.jj + 1 == cc.nti) {
-#pragma unroll
-                for (int i = 0; i < kPlanMaxAppends; ++i)
-                    first_holds |= i < plan_apps && plan_app_rh[i] == cc.r * Hkv + cc.h;
-            }
-            if (first_holds) store_all();
-            issue(ra, std::true_type{});
-            if (!first_holds) store_all();
-        } else {
-            issue(ra, std::true_type{});
-        }
+        if (!kDeferStores && holds_token(cc)) store_all();
+        issue(ra, std::true_type{});
+        if (!kDeferStores && !stored) store_all();
         enter();
         while (true) {
             if (nloaded < ntiles) {
