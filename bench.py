@@ -482,6 +482,36 @@ def run_workload(name, args, dev):
     return rec, w
 
 
+def read_probe_bandwidth(dev):
+    """HBM read bandwidth of the decode's access pattern: pa_read_probe over
+    4 GiB read as 4 KB chunks in a seeded random order (best of 3 launches,
+    HIP events on its stream).  Context for the roofline fractions, which
+    are taken against the published 8 TB/s."""
+    import torch
+    from paged_kv_cache_234_amd import pa_read_probe
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    ids = torch.as_tensor(np.random.default_rng(0).permutation(nbytes // 4096).astype(np.int32),
+                          device=dev)
+    props = torch.cuda.get_device_properties(dev)
+    sink = torch.empty(props.multi_processor_count * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    pa_read_probe(buf, ids, sink)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa_read_probe(buf, ids, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del buf, ids, sink
+    torch.cuda.empty_cache()
+    return nbytes / (best * 1e-3) / 1e9
+
+
 def copy_bandwidth(dev):
     """Achievable copy bandwidth in this process (context for the peak)."""
     import torch
@@ -527,6 +557,7 @@ def main(argv=None):
         del w
         recs[name] = rec
     copy_gbps = copy_bandwidth(dev)
+    probe_gbps = read_probe_bandwidth(dev)
 
     h = recs[headline]
     result = {
@@ -549,9 +580,15 @@ def main(argv=None):
         "kv_bytes_unique": h["kv_bytes_unique"],
         "launch": h["launch"],
         "decode_kernel_us": h["decode_kernel_us"],
+        "eager_event_us": h["eager_event_us"],
+        "plan_us": h["plan_us"],
         "copy_GBps": round(copy_gbps, 1),
+        "read_probe_GBps": round(probe_gbps, 1),
         "roofline": h["roofline"],
     }
+    for k in ("prefill_tflops", "prefill_mfma_frac_bf16"):
+        if k in h:
+            result[k] = h[k]
     if "cpu_baseline" in h:
         result["cpu_baseline"] = h["cpu_baseline"]
         result["cpu_baseline_1thread"] = h["cpu_baseline_1thread"]

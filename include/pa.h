@@ -387,6 +387,21 @@ pa_status_t pa_decode_noalloc(void* out, const void* q, pa_dtype_t q_dtype,
 size_t pa_decode_noalloc_max_bytes(void);
 
 /*
+ * Measurement aid, not part of the attention path: reads num_chunks 4 KB
+ * chunks of buf (chunk i at byte offset chunk_ids[i] * 4096) in that order,
+ * one workgroup of four wavefronts per compute unit, each wavefront keeping
+ * eight chunks in flight -- the access pattern of the decode's K/V block
+ * tiles.  Timing it gives the HBM read bandwidth this pattern can reach, the
+ * context for a roofline fraction taken against the published peak.  Every
+ * chunk id must be < bytes / 4096 (device contents are trusted).
+ *   sink   at least (compute units * 256) words; receives per-thread folds
+ *          of the data read (keeps the loads live), no meaning otherwise
+ */
+pa_status_t pa_read_probe(const void* buf, size_t bytes, const int32_t* chunk_ids,
+                          int32_t num_chunks, uint32_t* sink, size_t sink_bytes,
+                          hipStream_t stream);
+
+/*
  * Name of a status code: a static string, never NULL.  Every call above
  * reports an argument, shape or launch problem as a status the caller can
  * name, instead of falling back to another path (RustInfer, "Tensor

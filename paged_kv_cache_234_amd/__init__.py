@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     pa_decode_plan, pa_decode_plan_bytes, decode_plan_buffer,
     pa_decode_splitk_reduce, pa_prefill_chunk,
     pa_decode_workspace_bytes, pa_selftest, status_string, pa_decode_noalloc,
-    pa_decode_noalloc_max_bytes,
+    pa_decode_noalloc_max_bytes, pa_read_probe,
 )
 from .pool import KVPool  # noqa: F401

@@ -23,7 +23,7 @@ EXPORTED = (
     "pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade", "pa_decode_multi",
     "pa_decode_splitk_reduce", "pa_prefill_chunk", "pa_decode_plan", "pa_decode_plan_bytes",
     "pa_status_string", "pa_decode_workspace_bytes", "pa_selftest", "pa_decode_noalloc",
-    "pa_decode_noalloc_max_bytes",
+    "pa_decode_noalloc_max_bytes", "pa_read_probe",
 )
 
 _lib = None
@@ -72,6 +72,8 @@ def load(path=LIB_PATH):
     lib.pa_selftest.argtypes = []
     lib.pa_decode_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32,
                                       i32, i32, f32, i32, i32, st]
+    lib.pa_read_probe.argtypes = [vp, ctypes.c_size_t, vp, i32, vp, ctypes.c_size_t, st]
+    lib.pa_read_probe.restype = ctypes.c_int
     lib.pa_decode_noalloc_max_bytes.argtypes = []
     lib.pa_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     for fn in ("pa_kv_append", "pa_decode", "pa_decode_append", "pa_decode_cascade",
@@ -262,6 +264,15 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                   float(scale), int(partition_size), int(max_partitions),
                                   _stream(stream))
     _check("pa_decode_noalloc", st)
+
+
+def pa_read_probe(buf, chunk_ids, sink, stream=None):
+    """Read the 4 KB chunks of buf (a device tensor) in chunk_ids' order (a
+    measurement aid: the decode's block-tile access pattern)."""
+    nbytes = buf.numel() * buf.element_size()
+    st = load().pa_read_probe(_ptr(buf), nbytes, _i32(chunk_ids, "chunk_ids"), chunk_ids.numel(),
+                              _ptr(sink), sink.numel() * sink.element_size(), _stream(stream))
+    _check("pa_read_probe", st)
 
 
 def pa_decode_noalloc_max_bytes():

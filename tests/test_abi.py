@@ -204,3 +204,14 @@ def test_noalloc_rejects_bad_arguments_and_oversized_partials_before_any_device_
     # 8 x 32 heads x 512 partitions x 130 floats = 65 MiB of partials > 64 MiB
     assert _noalloc(lib, B=8, hq=32, hkv=8, pmax=512) == _lib.PA_ERR_TOO_LARGE
     assert _noalloc(lib, B=4096, hq=16, pmax=64) == _lib.PA_ERR_TOO_LARGE
+
+
+def test_read_probe_rejects_bad_arguments_before_any_launch():
+    lib = _lib.load()
+    probe = lambda buf, nbytes, ids, n, sink, sink_bytes: lib.pa_read_probe(
+        buf, nbytes, ids, n, sink, sink_bytes, None)
+    assert probe(None, 1 << 20, FAKE, 4, FAKE, 1 << 20) == _lib.PA_ERR_ARG
+    assert probe(FAKE, 1 << 20, FAKE, 0, FAKE, 1 << 20) == _lib.PA_ERR_ARG
+    assert probe(FAKE, 2048, FAKE, 1, FAKE, 1 << 20) == _lib.PA_ERR_ARG          # < one chunk
+    assert probe(FAKE, 1 << 20, FAKE, 257, FAKE, 1 << 20) == _lib.PA_ERR_ARG     # > 256 chunks
+    assert probe(FAKE, 1 << 20, FAKE, 4, FAKE, 64) == _lib.PA_ERR_ARG            # sink too small
