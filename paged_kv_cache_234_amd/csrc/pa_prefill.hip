@@ -185,12 +185,128 @@ template <int D> struct StagedOps : TileOps<kBF16, D> {
                     s[n][i] = mfma_bf16(as_bf16x8(r.k[i][k]), q[n].op[k], s[n][i]);
             }
     }
-    // O^T of one query tile from its probabilities
-    __device__ static void pv_column(const Regs& r, const float (&p)[NMT][4], f32x4 (&o)[NVT]) {
+    // O^T of one query tile from its probabilities, and the column sums of
+    // the same bf16 probabilities on the matrix core: an all-ones A operand
+    // gives every row of the 16x16 result the sum over the 32 keys, so the
+    // normaliser needs no VALU adds and no exchange between lane groups
+    __device__ static void pv_column(const Regs& r, const float (&p)[NMT][4], f32x4 (&o)[NVT],
+                                     f32x4& lsum) {
         const bf16x8 b = as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
 #pragma unroll
         for (int t = 0; t < NVT; ++t) o[t] = mfma_bf16(as_bf16x8(r.v[t]), b, o[t]);
+        constexpr uint32_t kOne2 = 0x3F803F80u;              // two bf16 1.0
+        lsum = mfma_bf16(as_bf16x8(u32x4{kOne2, kOne2, kOne2, kOne2}), b, lsum);
+    }
+};
+
+// Online softmax of the staged prefill: NC 16-column query tiles per
+// wavefront, scores folded into the exponent as exp2(s * c - mr) (c > 0).
+//
+// The reference mr of a column moves only when a score exceeds it by more
+// than kRescaleSlack (log2 units); between moves the exponent offset -mr and
+// the raw-score threshold thr = (mr + slack) / c are constants, so the common
+// tile costs each lane one maximum over its own 8 scores and one compare,
+// and a wave-wide ballot decides whether any column must move.  Only then is
+// the column maximum formed across the four lane groups.  A move happens
+// exactly when the tile holds a score above mr + slack, so that tile's
+// maximum is the running maximum and becomes the new reference.  The row
+// sums l are accumulated on the matrix core from the same bf16 probabilities
+// the PV product uses.
+template <int D, int NC> struct StagedSoftmax {
+    using Ops = StagedOps<D>;
+    static constexpr int NMT = Ops::NMT, NVT = Ops::NVT;
+    float mr[NC], thr[NC], nref[NC];
+    f32x4 o[NC][NVT];
+    f32x4 lsum[NC];
+
+    __device__ void init() {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            mr[n] = -INFINITY;
+            thr[n] = -INFINITY;
+            nref[n] = 0.f;
+            lsum[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) o[n][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // move column n's reference to the tile maximum where it exceeds thr
+    __device__ void bump(int n, float lmax, float c) {
+        const float tmax = max_over_groups_nan(lmax);        // the column's tile maximum
+        const bool move = tmax > thr[n];
+        const float mr_new = move ? tmax * c : mr[n];
+        // a column that has seen nothing yet (mr = -inf) scales by 0
+        const float alpha = move ? fast_exp2(mr[n] - mr_new) : 1.0f;
+        mr[n] = mr_new;
+        thr[n] = move ? (mr_new + kRescaleSlack) / c : thr[n];
+        nref[n] = mr_new == -INFINITY ? 0.f : -mr_new;
+        lsum[n] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) o[n][t] *= alpha;
+    }
+
+    // One 32-position half for all NC query tiles.  vsrc: the half's staged
+    // V; limit[n]: this lane's last visible position in query tile n
+    // (relative to the half); nvalid: real tokens in the half; masked: some
+    // position of some tile needs masking.  The V operand is read from LDS
+    // once QK^T has consumed the K registers, which keeps the wavefront
+    // within the register budget of two wavefronts per SIMD.  The reference
+    // test of every tile comes first, so that from the exponentials on the
+    // half is one branch-free stretch.  The PV products run at raised wave
+    // priority, so that the other wavefront on the SIMD issues its VALU work
+    // while they occupy the matrix core (about 1.5% faster in a same-box A/B).
+    __device__ void step(typename Ops::Regs& r, const char* vsrc, const typename Ops::Q (&q)[NC],
+                         float c, int nvalid, const int (&limit)[NC], bool masked, int lane) {
+        const int grp = lane >> 4;
+        f32x4 s4[NC][NMT];
+        Ops::template qk<NC>(r, q, s4);
+#pragma unroll
+        for (int v = 0; v < NVT; ++v)
+            r.v[v] = *reinterpret_cast<const u32x4*>(vsrc + ((v * 4 + grp) * 16 + (lane & 15)) * 16);
+        // V of positions past the context may hold any bits (NaN included)
+        if (masked && nvalid < 32) Ops::mask_v(r, nvalid, lane);
+        float s[NC][NMT][4];
+        float lmax[NC];
+        bool over = false;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+#pragma unroll
+            for (int i = 0; i < NMT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[n][i][e] = s4[n][i][e];
+            if (masked) {
+                // -inf: excluded from the maximum, and exp2(fma(-inf, c, .)) = 0
+                const int lim = min(limit[n], nvalid - 1);
+#pragma unroll
+                for (int i = 0; i < NMT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[n][i][e] = Ops::pos(i, e, grp) <= lim ? s[n][i][e] : -INFINITY;
+            }
+            lmax[n] = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NMT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lmax[n] = fmax_nan(lmax[n], s[n][i][e]);
+            over |= lmax[n] > thr[n];
+        }
+        if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n) bump(n, lmax[n], c);
+        }
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            float p[NMT][4];
+#pragma unroll
+            for (int i = 0; i < NMT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[i][e] = fast_exp2(__builtin_fmaf(s[n][i][e], c, nref[n]));
+            __builtin_amdgcn_s_setprio(1);
+            Ops::pv_column(r, p, o[n], lsum[n]);
+            __builtin_amdgcn_s_setprio(0);
+        }
     }
 };
 
@@ -202,6 +318,12 @@ template <int D> struct StagedOps : TileOps<kBF16, D> {
 // longest items share a CU with the shortest (longest-processing-time order).
 // Every (chunk, row group) class's count is held in registers, 64 per
 // register: up to 64 * kOrderGroups classes, else the natural order.
+//
+// Blocks are dealt round-robin to the 8 XCDs (block b to XCD b % 8), each
+// with its own L2.  When the KV heads divide by 8, XCD x takes every item of
+// KV heads x, x + 8, ..., ranked the same way over its own blocks and CUs:
+// all row groups of one (chunk, KV head) then read their K/V through one L2,
+// and each XCD gets the same mix of item sizes.
 constexpr int kOrderGroups = 8;
 
 __device__ __forceinline__ int launch_rank(int b, int nblocks, int stride) {
@@ -210,9 +332,10 @@ __device__ __forceinline__ int launch_rank(int b, int nblocks, int stride) {
     return p * stride + ((p & 1) ? m - 1 - pos : pos);
 }
 
-// (chunk c, KV head h, row group tg) of the item at rank r; false: no work
-__device__ bool item_at_rank(const PrefillArgs& a, int rows, int r, int lane, int& c, int& h,
-                             int& tg) {
+// (chunk c, KV head h, row group tg) of the item at rank r among the items of
+// KV heads h0 + hstep * j, j < nh; false: no work
+__device__ bool item_at_rank(const PrefillArgs& a, int rows, int r, int lane, int h0, int hstep,
+                             int nh, int& c, int& h, int& tg) {
     const int wpg = a.wg_per_head, ncls = a.num_chunks * wpg;
     int cost[kOrderGroups];                    // tiles of class 64 g + lane (0: no rows)
 #pragma unroll
@@ -238,18 +361,27 @@ __device__ bool item_at_rank(const PrefillArgs& a, int rows, int r, int lane, in
             if (g < ngroups) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(cost[g] >= x));
         return n;
     };
-    const int H = a.num_kv_heads;
+    const int H = nh;
+    // the search below only needs the bits of the largest count
+    int cmax = 0;
+#pragma unroll
+    for (int g = 0; g < kOrderGroups; ++g) cmax = max(cmax, cost[g]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cmax = max(cmax, __shfl_xor(cmax, off));
+    cmax = __builtin_amdgcn_readfirstlane(cmax);
+    if (cmax == 0) return false;
     // the item's tile count: the largest x with H * count_ge(x) > r
     int x = 0;
-    for (int bit = 25; bit >= 0; --bit) {
+    for (int bit = 31 - __builtin_clz(cmax); bit >= 0; --bit) {
         const int cand = x | (1 << bit);
         if ((long)H * count_ge(cand) > r) x = cand;
     }
     if (x == 0) return false;
     const int above = count_ge(x + 1), ncl = count_ge(x) - above;
     const int j = r - H * above;               // among the H * ncl items with x tiles
-    h = j / ncl;
-    int k = j - h * ncl;                       // the k-th class with x tiles, by index
+    const int hh = j / ncl;
+    h = h0 + hstep * hh;
+    int k = j - hh * ncl;                      // the k-th class with x tiles, by index
     int cls = 0;
 #pragma unroll
     for (int g = 0; g < kOrderGroups; ++g) {
@@ -289,8 +421,13 @@ void prefill_lds_kernel(PrefillArgs a) {
     int c, h, tg;
     if (a.num_cus > 0 && a.num_chunks * a.wg_per_head <= 64 * kOrderGroups) {
         // every wavefront finds the same item (wave-uniform ballots)
-        if (!item_at_rank(a, wg_rows, launch_rank(blockIdx.x, gridDim.x, a.num_cus), lane, c, h,
-                          tg))
+        constexpr int kXcd = 8;
+        const bool per_xcd = a.num_kv_heads % kXcd == 0 && a.num_cus % kXcd == 0;
+        const int xcd = blockIdx.x % kXcd;
+        const int rank = per_xcd ? launch_rank(blockIdx.x / kXcd, gridDim.x / kXcd, a.num_cus / kXcd)
+                                 : launch_rank(blockIdx.x, gridDim.x, a.num_cus);
+        if (!item_at_rank(a, wg_rows, rank, lane, per_xcd ? xcd : 0, per_xcd ? kXcd : 1,
+                          per_xcd ? a.num_kv_heads / kXcd : a.num_kv_heads, c, h, tg))
             return;                                       // the whole workgroup
         c = __builtin_amdgcn_readfirstlane(c);
         h = __builtin_amdgcn_readfirstlane(h);
@@ -355,9 +492,18 @@ void prefill_lds_kernel(PrefillArgs a) {
 
     // ---- staging: wavefront w moves block w of tile t --------------------------
     u32x4 sk[NLD], sv[NLD];
+    // physical ids of the blocks this wavefront stages, one tile per lane:
+    // lane j holds block 4 (ids_t0 + j) + wave (clamped to the last), so no
+    // memory latency sits between two tiles' loads
+    int ids = 0, ids_t0 = 0;
+    auto fetch_ids = [&](int t0) {
+        ids_t0 = t0;
+        ids = bt[min(4 * (t0 + lane) + wave, last_blk)];
+    };
+    fetch_ids(0);
     auto stage_load = [&](int t) {
-        const int lb = min(t * 4 + wave, last_blk);
-        const long phys = load_invariant(bt + __builtin_amdgcn_readfirstlane(lb));
+        if (t - ids_t0 >= kWave) fetch_ids(t);
+        const long phys = __builtin_amdgcn_readlane(ids, t - ids_t0);
         const char* kb = kbase + phys * blk_stride;
         const char* vb = vbase + phys * blk_stride;
         // ordinary (temporal) loads: the row groups of one (chunk, KV head)
@@ -404,7 +550,7 @@ void prefill_lds_kernel(PrefillArgs a) {
         }
     };
 
-    WaveSoftmax<kBF16, D, NC, SOps, true> st;
+    StagedSoftmax<D, NC> st;
     st.init();
     auto compute = [&](int buf, int t) {
 #pragma unroll
@@ -419,15 +565,12 @@ void prefill_lds_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int k = 0; k < NS; ++k)
                     r.k[i][k] = *reinterpret_cast<const u32x4*>(ks + i * KB + ((4 * k + grp) * 16 + g) * 16);
-#pragma unroll
-            for (int v = 0; v < NVT; ++v)
-                r.v[v] = *reinterpret_cast<const u32x4*>(vs + ((v * 4 + grp) * 16 + g) * 16);
             const int nvalid = min(kend - t0, 32);
             const bool masked = (t0 + 31 > min_last) || (nvalid < 32);
             int limit[NC];
 #pragma unroll
             for (int n = 0; n < NC; ++n) limit[n] = my_last[n] - t0;
-            st.step(r, qop, cs, nvalid, limit, masked, lane);
+            st.step(r, vs, qop, cs, nvalid, limit, masked, lane);
         }
     };
 
@@ -444,7 +587,7 @@ void prefill_lds_kernel(PrefillArgs a) {
     const float vsc = KIND == kFP8 ? load_invariant(a.v_scale + h) : 1.0f;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-        const float l = sum_over_groups(st.l[n]);        // against the reference mr
+        const float l = st.lsum[n][0];                   // against the reference mr
         if (!col_valid[n]) continue;
         const float inv = vsc / l;
         const long orow =
