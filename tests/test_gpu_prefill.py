@@ -126,3 +126,19 @@ def test_prefill_launch_order_many_chunks(cache, nchunks):
     kp, vp = oracle_pool(w)
     err = max_abs_err(as_f64(out), _oracle(w, kp, vp))
     assert err <= TOL[cache], err
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 2)])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_prefill_long_prefix(cache, hq, hkv):
+    """Chunks after 4,100-9,000 cached tokens: a workgroup stages more than 64
+    tiles, so its per-lane register of block ids is refilled, and the launch
+    ranking searches tile counts past 128.  With 8 KV heads the ranking runs
+    per XCD."""
+    chunks = [(9000, 40), (4100, 17), (0, 24), (6000, 1)]
+    w = _case(cache, hq, hkv, 128, chunks, seed=77 + hkv)
+    out = run_prefill(w, gpu_pool(w))
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    err = max_abs_err(as_f64(out), _oracle(w, kp, vp))
+    assert err <= TOL[cache], err
