@@ -343,6 +343,9 @@ pa_status_t pa_decode_splitk_reduce(void* out, pa_dtype_t out_dtype,
  * to positions 0 .. P_c + i.
  *   out, q         [query_start_loc[num_chunks]][num_heads][head_dim]
  *   block_tables   [num_chunks][max_blocks_per_seq]
+ * A context length is taken as at most max_blocks_per_seq * block_size, as
+ * in pa_decode: positions past the block-table row are never read.  A chunk
+ * whose rows then outnumber its context (C_c > context) writes nothing.
  */
 pa_status_t pa_prefill_chunk(void* out, const void* q, pa_dtype_t q_dtype,
                              const int32_t* query_start_loc, int32_t num_chunks,

@@ -67,7 +67,8 @@ void prefill_kernel(PrefillArgs a) {
 
     const int q0 = a.query_start_loc[c];
     const int C = a.query_start_loc[c + 1] - q0;
-    const int L = a.context_lens[c];
+    // positions past the chunk's block-table row are never read
+    const int L = min(a.context_lens[c], a.max_blocks_per_seq * kBlock);
     const int P = L - C;
     const int npos = a.npos;
     const int row0 = (tg * NW + wave) * NC * npos;       // first chunk row of this wavefront
@@ -346,7 +347,7 @@ __device__ bool item_at_rank(const PrefillArgs& a, int rows, int r, int lane, in
             const int cc = cls / wpg, t = cls - cc * wpg;
             const int q0 = a.query_start_loc[cc];
             const int C = a.query_start_loc[cc + 1] - q0;
-            const int P = a.context_lens[cc] - C;
+            const int P = min(a.context_lens[cc], a.max_blocks_per_seq * kBlock) - C;
             if (P >= 0 && t * rows < C) {
                 const int kend = P + min(C, rows * (t + 1));
                 cost[g] = (kend - 1) / kLdsTile + 1;
@@ -441,7 +442,8 @@ void prefill_lds_kernel(PrefillArgs a) {
 
     const int q0 = a.query_start_loc[c];
     const int C = a.query_start_loc[c + 1] - q0;
-    const int L = a.context_lens[c];
+    // positions past the chunk's block-table row are never read
+    const int L = min(a.context_lens[c], a.max_blocks_per_seq * kBlock);
     const int P = L - C;
     const int npos = a.npos;
     const int wg_row0 = tg * wg_rows;

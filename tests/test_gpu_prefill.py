@@ -142,3 +142,21 @@ def test_prefill_long_prefix(cache, hq, hkv):
     kp, vp = oracle_pool(w)
     err = max_abs_err(as_f64(out), _oracle(w, kp, vp))
     assert err <= TOL[cache], err
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_prefill_context_beyond_the_table_is_clamped(cache):
+    """A context length past max_blocks_per_seq * 16 is taken as that bound,
+    as in pa_decode, so nothing past the chunk's block-table row is read: a
+    chunk whose real context fills its row gives the same bits when its
+    context length is stated larger."""
+    w = _case(cache, 8, 2, 128, [(100, 28)], seed=9)
+    assert w.chunk_block_tables.shape[1] * 16 == int(w.chunk_context_lens[0]) == 128
+    pool = gpu_pool(w)
+    ref = run_prefill(w, pool)
+    qp = w.q_prefill.cuda().contiguous()
+    out = torch.full_like(qp, float("nan"))
+    pa_prefill_chunk(out, qp, i32(w.query_start_loc), 28, pool.k, pool.v,
+                     i32(w.chunk_block_tables), i32([200]), w.scale, pool.k_scale, pool.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
