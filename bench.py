@@ -276,10 +276,15 @@ class LayerStep:
         if ev is not None:
             ev[3].record(stream)
         if self.has_prefill:
-            pa_prefill_chunk(self.outp, self.qp, self.pqsl, self.maxq, pool.k, pool.v, self.cbt,
-                             self.clens, w.scale, pool.k_scale, pool.v_scale)
+            self.prefill_only(layer)
             if ev is not None:
                 ev[4].record(stream)
+
+    def prefill_only(self, layer, base=None):
+        from paged_kv_cache_234_amd import pa_prefill_chunk
+        w, pool = self.w, self.pools[layer % self.R]
+        pa_prefill_chunk(self.outp, self.qp, self.pqsl, self.maxq, pool.k, pool.v, self.cbt,
+                         self.clens, w.scale, pool.k_scale, pool.v_scale)
 
     def decode_only(self, layer, base=None):
         from paged_kv_cache_234_amd import (pa_decode, pa_decode_append, pa_decode_cascade,
@@ -361,6 +366,7 @@ def run_workload(name, args, dev):
         g_warm = captured(step, 0, warm)
         g_steps = captured(step, args.warmup, args.steps)
         g_decode = captured(decode_only, args.warmup, args.steps)
+        g_prefill = captured(ls.prefill_only, args.warmup, args.steps) if has_prefill else None
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         g_warm.replay()
@@ -392,6 +398,20 @@ def run_workload(name, args, dev):
     d1.record(stream)
     torch.cuda.synchronize()
     decode_ms = d0.elapsed_time(d1) / args.steps
+
+    # ---- the prefill kernel alone, the same way (mixed workload) -----------
+    prefill_ms = None
+    if has_prefill:
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        if args.eager:
+            steps_of(ls.prefill_only, args.warmup, args.steps)
+        else:
+            g_prefill.replay()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        prefill_ms = f0.elapsed_time(f1) / args.steps
 
     # ---- per-kernel durations, eager, HIP events around each launch ---------
     nev = 5 if has_prefill else 4
@@ -471,12 +491,13 @@ def run_workload(name, args, dev):
         },
     }
     if has_prefill:
-        pf_ms = kern_ms["prefill_chunk"]
-        rec["prefill_tflops"] = round(w.prefill_flops() / (pf_ms * 1e-3) / 1e12, 2)
+        # K back-to-back graph-replayed launches, as for the decode kernel
+        rec["prefill_kernel_us"] = round(prefill_ms * 1e3, 3)
+        rec["prefill_tflops"] = round(w.prefill_flops() / (prefill_ms * 1e-3) / 1e12, 2)
         rec["prefill_mfma_frac_bf16"] = round(rec["prefill_tflops"] / 2500.0, 4)
     del ls
     if not args.eager:
-        del g_warm, g_steps, g_decode
+        del g_warm, g_steps, g_decode, g_prefill
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec, w
@@ -586,7 +607,7 @@ def main(argv=None):
         "read_probe_GBps": round(probe_gbps, 1),
         "roofline": h["roofline"],
     }
-    for k in ("prefill_tflops", "prefill_mfma_frac_bf16"):
+    for k in ("prefill_kernel_us", "prefill_tflops", "prefill_mfma_frac_bf16"):
         if k in h:
             result[k] = h[k]
     if "cpu_baseline" in h:

@@ -308,14 +308,9 @@ template <int D> struct TileOps<kF32, D> {
 // finish() re-expresses l against the true max.
 constexpr float kRescaleSlack = 8.0f;
 
-// OpsT: the tile operations (key order of the score registers, the PV
-// operand exchange).  FOLD: the score multiplier c is folded into the
-// exponent, exp2(s * c - ref) as one fma, and the tile maximum is taken over
-// raw scores and scaled once (c * max s = max c * s for c > 0: rounding is
-// monotonic); the caller then guarantees c > 0.
-template <int KIND, int D, int NC = 1, class OpsT = TileOps<KIND, D>, bool FOLD = false>
+template <int KIND, int D, int NC = 1>
 struct WaveSoftmax {
-    using Ops = OpsT;
+    using Ops = TileOps<KIND, D>;
     static constexpr int NMT = Ops::NMT, NVT = Ops::NVT, TT = Ops::TT;
     float m[NC], mr[NC], l[NC];
     f32x4 o[NC][NVT];
@@ -343,17 +338,6 @@ struct WaveSoftmax {
         Ops::template qk<NC>(r, q, s4);
         if (masked && nvalid < TT) Ops::mask_v(r, nvalid, lane);
         float p[NC][NMT][4];
-        if constexpr (FOLD) {
-            // query tile by query tile: tile n's PV MFMAs run while tile
-            // n + 1's softmax is computed (and QK of the later tiles while
-            // tile 0's is)
-#pragma unroll
-            for (int n = 0; n < NC; ++n) {
-                fold_column(n, s4[n], p[n], c, nvalid, limit[n], masked, grp);
-                Ops::pv_column(r, p[n], o[n]);
-            }
-            return;
-        }
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
             float s[NMT][4];
@@ -406,40 +390,6 @@ struct WaveSoftmax {
 #pragma unroll
             for (int t = 0; t < NVT; ++t) o[n][t] *= alpha;
         }
-    }
-
-    __device__ void fold_column(int n, const f32x4 (&s4)[NMT], float (&p)[NMT][4], float c,
-                                int nvalid, int limit, bool masked, int grp) {
-        float s[NMT][4];
-#pragma unroll
-        for (int i = 0; i < NMT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[i][e] = s4[i][e];
-        if (masked) {
-            // -inf: excluded from the max, and exp2(fma(-inf, c, .)) = 0
-            const int lim = min(limit, nvalid - 1);
-#pragma unroll
-            for (int i = 0; i < NMT; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[i][e] = Ops::pos(i, e, grp) <= lim ? s[i][e] : -INFINITY;
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NMT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tmax = fmax_nan(tmax, s[i][e]);
-        rescale(n, max_over_groups_nan(tmax) * c);            // -inf stays -inf (c > 0)
-        const float nref = (mr[n] == -INFINITY) ? 0.f : -mr[n];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < NMT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p[i][e] = fast_exp2(__builtin_fmaf(s[i][e], c, nref));
-                psum += p[i][e];
-            }
-        l[n] += psum;
     }
 };
 
