@@ -148,7 +148,7 @@ constexpr int kWideItemCost = 1;
 // NC * 16 / G members or query positions.
 // PLAIN: sequence rows only (pa_decode); the group and multi-query row code
 // is compiled out.
-template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE>
+template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE, bool CI = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
     // which rows a plan describes: plain sequences, cascade or multi-query
@@ -305,6 +305,56 @@ void decode_kernel(DecodeArgs a) {
     };
     // plain decode keeps it in s_aux (otherwise unused) once the prefix is built
     auto row_head_tiles = [&](int r) { return PLAIN ? s_aux[r] : head_tiles_of(r); };
+    // Tile order within a row.  Sequence and group rows: virtual head (KV
+    // head h, member chunk ch: vh = h nch + ch), then item (partition).
+    // Multi-query launches (CI): KV head, then item, then chunk, so a row
+    // whose query columns take nch > 1 chunks per KV head has the chunks of
+    // one partition next to each other: neighbouring wavefronts stream the
+    // same K/V tiles at the same time and the second read comes from L2.
+    // Every item of a partition but the last has tpi tiles, those of the
+    // last rem.  The item of row r holding tile g: its first tile t0, its
+    // tiles nti, virtual head vh, item p and tile jj within it.
+    auto locate = [&](int g, int r, int& t0, int& nti, int& vh, int& p, int& jj) {
+        const int th = row_head_tiles(r);
+        const int base = s_tpre[r];
+        if constexpr (PLAIN || !CI) {                              // virtual head, then item
+            vh = (g - base) / th;
+            const int j = g - base - vh * th;
+            p = j / tpi;
+            t0 = base + vh * th + p * tpi;
+            jj = j - p * tpi;
+            nti = p + 1 < row_items(r) ? tpi : th - p * tpi;
+            return;
+        }
+        const int nch = row_heads(r) / Hkv;
+        const int n = row_items(r);
+        const int rem = th - (n - 1) * tpi;
+        const int hb = nch * th;                                   // tiles of one KV head
+        const int h = (g - base) / hb;
+        const int jh = g - base - h * hb;
+        const int full = (n - 1) * nch * tpi;                      // tiles of the full items
+        int ch;
+        if (jh < full) {
+            p = jh / (nch * tpi);
+            const int k = jh - p * nch * tpi;
+            ch = k / tpi;
+            jj = k - ch * tpi;
+            t0 = base + h * hb + p * nch * tpi + ch * tpi;
+            nti = tpi;
+        } else {
+            p = n - 1;
+            const int k = jh - full;
+            ch = k / rem;
+            jj = k - ch * rem;
+            t0 = base + h * hb + full + ch * rem;
+            nti = rem;
+        }
+        vh = h * nch + ch;
+    };
+    auto item_holding = [&](int g, int r, int& t0, int& nti) {
+        int vh, p, jj;
+        locate(g, r, t0, nti, vh, p, jj);
+    };
 
     // single pass: sequences with L = 0 have no tile; their rows are zeros
     auto zero_empty_rows = [&]() {
@@ -434,13 +484,9 @@ void decode_kernel(DecodeArgs a) {
     auto row_of2 = [&](int ga, int gb, int& ra, int& rb) { row_of2_in(s_tpre, ga, gb, ra, rb); };
     // the item start nearest to tile g < T in row r (the earlier one on a tie)
     auto nearest_item_start = [&](int g, int r) -> int {
-        const int th = row_head_tiles(r);
-        const int base = s_tpre[r];
-        const int vh = (g - base) / th;
-        const int head0 = base + vh * th;
-        const int p = (g - head0) / tpi;
-        const int before = head0 + p * tpi;                        // item holding g
-        const int after = p + 1 < row_items(r) ? before + tpi : head0 + th;
+        int before, nti;
+        item_holding(g, r, before, nti);
+        const int after = before + nti;
         return (g - before <= after - g) ? before : after;
     };
     // X k / NWG, exact: the double product is below 2^53 and a non-integral
@@ -462,34 +508,47 @@ void decode_kernel(DecodeArgs a) {
         // wavefronts split that run into equal costs (at tile granularity)
         const int C = total_cost;
         const int ci = tpi + kItemCost;                   // cost of a full item
-        struct HeadAt {
-            int tile0, cost0, th, n, o, p;                // head's first tile / cost; offset o
+        // the item of row r holding cost c, in the tile order above: its KV
+        // head's first tile and cost, the offset o of c in the head, and the
+        // item's first tile, first cost and tiles relative to the head
+        struct ItemAt {
+            int tile0, cost0, o, it_t0, it_c0, nti;
         };
-        auto head_at = [&](int c, int r) {                // the (virtual) head of row r holding cost c
-            HeadAt h;
-            h.th = head_tiles_of(r);
-            h.n = row_items(r);
-            const int ch = h.th + kItemCost * h.n;
-            const int vh = (c - s_cpre[r]) / ch;
-            h.tile0 = s_tpre[r] + vh * h.th;
-            h.cost0 = s_cpre[r] + vh * ch;
-            h.o = c - h.cost0;
-            h.p = min(h.o / ci, h.n - 1);
-            return h;
+        auto item_at_cost = [&](int c, int r) {
+            ItemAt it;
+            const int th = head_tiles_of(r), n = row_items(r);
+            const int nch = CI ? row_heads(r) / Hkv : 1;      // (otherwise each virtual head is a unit)
+            const int rem = th - (n - 1) * tpi;
+            const int chead = nch * (th + kItemCost * n);         // cost of one KV head
+            const int h = (c - s_cpre[r]) / chead;
+            it.tile0 = s_tpre[r] + h * nch * th;
+            it.cost0 = s_cpre[r] + h * chead;
+            it.o = c - it.cost0;
+            const int full_c = (n - 1) * nch * ci;                // cost of the full items
+            if (it.o < full_c) {
+                const int k = it.o / ci;
+                it.it_c0 = k * ci;
+                it.it_t0 = k * tpi;
+                it.nti = tpi;
+            } else {
+                const int cr = rem + kItemCost;
+                const int j = min((it.o - full_c) / cr, nch - 1);
+                it.it_c0 = full_c + j * cr;
+                it.it_t0 = (n - 1) * nch * tpi + j * rem;
+                it.nti = rem;
+            }
+            return it;
         };
         auto nearest_item_by_cost = [&](int c, int r, int& tile, int& cost) {
-            const HeadAt h = head_at(c, r);
-            const int before = h.p * ci;
-            const bool last = h.p + 1 == h.n;
-            const int after = last ? h.th + kItemCost * h.n : before + ci;
-            const bool take_before = h.o - before <= after - h.o;
-            tile = h.tile0 + (take_before ? h.p * tpi : (last ? h.th : (h.p + 1) * tpi));
-            cost = h.cost0 + (take_before ? before : after);
+            const ItemAt it = item_at_cost(c, r);
+            const int before = it.it_c0, after = it.it_c0 + it.nti + kItemCost;
+            const bool take_before = it.o - before <= after - it.o;
+            tile = it.tile0 + it.it_t0 + (take_before ? 0 : it.nti);
+            cost = it.cost0 + (take_before ? before : after);
         };
         auto tile_at_cost = [&](int c, int r) {           // inside an item, or its successor's start
-            const HeadAt h = head_at(c, r);
-            const int nt = h.p + 1 < h.n ? tpi : h.th - h.p * tpi;
-            return h.tile0 + h.p * tpi + min(h.o - h.p * ci, nt);
+            const ItemAt it = item_at_cost(c, r);
+            return it.tile0 + it.it_t0 + min(it.o - it.it_c0, it.nti);
         };
         int ca = 0, ce = 0;
         const int sa = share(C, blockIdx.x), se = share(C, blockIdx.x + 1);
@@ -613,13 +672,32 @@ void decode_kernel(DecodeArgs a) {
     auto advance = [&](Cursor& c) {
         if (++c.jj < c.nti) return;
         const long t0 = c.t0 + c.nti;
-        int r = c.r, vh = c.vh, p = c.p + 1;
-        if (p == c.n) {
-            p = 0;
-            if (++vh == c.nh) {
-                vh = 0;
-                do { ++r; } while (s_tpre[r + 1] == s_tpre[r]);    // skip rows without tiles
+        int r = c.r, vh = c.vh, p = c.p;
+        if constexpr (PLAIN || !CI) {               // item, then virtual head, then row
+            if (++p == c.n) {
+                p = 0;
+                if (++vh == c.nh) {
+                    vh = 0;
+                    do { ++r; } while (s_tpre[r + 1] == s_tpre[r]);    // skip rows without tiles
+                }
             }
+        } else {
+            // skip rows without tiles (bounded: a bad cursor cannot run away)
+            auto next_row = [&]() { do { ++r; } while (r < R - 1 && s_tpre[r + 1] == s_tpre[r]); };
+            // member chunk, then item, then KV head, then row (the order above)
+            const int nch = c.nh / Hkv;
+            int h = c.h, ch = c.ch;
+            if (++ch == nch) {
+                ch = 0;
+                if (++p == c.n) {
+                    p = 0;
+                    if (++h == Hkv) {
+                        h = 0;
+                        next_row();
+                    }
+                }
+            }
+            vh = h * nch + ch;
         }
         c.jj = 0;
         set_item(c, r, vh, p, t0);
@@ -634,13 +712,10 @@ void decode_kernel(DecodeArgs a) {
 
     // cursor at tile g of row r
     auto cursor_at = [&](Cursor& c, int g, int r) __attribute__((always_inline)) {
-        const int th = row_head_tiles(r);
-        const int base = s_tpre[r];
-        const int vh = (g - base) / th;
-        const int j = g - base - vh * th;
-        const int p = j / tpi;
-        set_item(c, r, vh, p, base + vh * th + p * tpi);
-        c.jj = j - p * tpi;
+        int t0, nti, vh, p, jj;
+        locate(g, r, t0, nti, vh, p, jj);
+        set_item(c, r, vh, p, t0);
+        c.jj = jj;
     };
 
     // ---- the range in processing order: Y, M, X ----------------------------
@@ -1097,7 +1172,7 @@ void decode_kernel(DecodeArgs a) {
     }
 }
 
-template <int KIND, int D, int NC, bool PLAIN, int MODE = kRun>
+template <int KIND, int D, int NC, bool PLAIN, int MODE = kRun, bool CI = false>
 static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
     constexpr int NW = 4;
     int dev = 0, cus = 256;
@@ -1107,7 +1182,7 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     long grid = (long)cus * waves_per_simd(KIND, D);
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
-    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE>), dim3((unsigned)grid), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE, CI>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -1121,10 +1196,14 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     auto tiles = [&](int tt) { return items_bound * ((a.partition_size + tt - 1) / tt); };
     // tile numbers are 32-bit in the kernel
     if (tiles(16) > 0x7fffffffL) return PA_ERR_UNSUPPORTED;
+    // multi-query rows take the chunk-inner tile order (CI)
+    const bool ci = a.query_start_loc != nullptr;
+#define PA_WIDE(K, DD, TT, CIV)                                                               \
+    (a.plan_out ? launch_decode<K, DD, 2, false, kMakePlan, CIV>(a, tiles(TT), stream)        \
+     : a.plan   ? launch_decode<K, DD, 2, false, kUsePlan, CIV>(a, tiles(TT), stream)         \
+                : launch_decode<K, DD, 2, false, kRun, CIV>(a, tiles(TT), stream))
 #define PA_LAUNCH(K, DD, TT)                                                          \
-    (wide ? (a.plan_out ? launch_decode<K, DD, 2, false, kMakePlan>(a, tiles(TT), stream) \
-             : a.plan   ? launch_decode<K, DD, 2, false, kUsePlan>(a, tiles(TT), stream)  \
-                        : launch_decode<K, DD, 2, false>(a, tiles(TT), stream))           \
+    (wide ? (ci ? PA_WIDE(K, DD, TT, true) : PA_WIDE(K, DD, TT, false))              \
           : (a.plan_out ? launch_decode<K, DD, 1, true, kMakePlan>(a, tiles(TT), stream)  \
              : a.plan   ? launch_decode<K, DD, 1, true, kUsePlan>(a, tiles(TT), stream)   \
                         : launch_decode<K, DD, 1, true>(a, tiles(TT), stream)))
@@ -1136,6 +1215,7 @@ static pa_status_t run_decode(const DecodeArgs& a, pa_dtype_t cache_dtype, int h
     else if (kind == kF32 && head_dim == 64) e = PA_LAUNCH(kF32, 64, 16);
     else return PA_ERR_UNSUPPORTED;
 #undef PA_LAUNCH
+#undef PA_WIDE
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
