@@ -130,3 +130,19 @@ def test_planned_spec_verify_full_size_repeats_exactly():
     want, _, _ = run_multi(w, pool, 256)
     g, r = as_f64(out1), as_f64(want)
     assert np.max(np.abs(g - r)) <= TOL[w.cache_dtype]
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_planned_equals_unplanned_bit_exact(cache):
+    """A plan assigns items to wavefronts by cost, an unplanned launch by
+    tiles; each item is computed the same way wherever it runs (cut items are
+    handed on, not merged), so at one partition size the outputs and every
+    partial agree bit for bit, with several 32-column chunks per KV head."""
+    w = _case(cache, 16, 2, 128, CHUNKS, seed=41)
+    pool = gpu_pool(w)
+    a_out, a_parts, _ = run_multi(w, pool, 64, planned=True)
+    b_out, b_parts, _ = run_multi(w, pool, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(a_out, b_out)
+    for x, y in zip(a_parts, b_parts):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
