@@ -60,7 +60,7 @@ PLAN_LAYERS = 32
 # 1024 for the fp8 mixed batch (16 tiles of 64 tokens per item: at 256 the
 # per-item cost of 4-tile items dominates), 512 for draft verification; the
 # tiny fp32 batch uses one-tile items, which no wavefront shares
-DEFAULT_PS = {1: 16, 2: 256, 3: 256, 4: 512, 5: 1024}
+DEFAULT_PS = {1: 16, 2: 512, 3: 256, 4: 512, 5: 1024}
 SPEC_VERIFY_PS = 512
 HEADLINE = "long-context-bf16-splitk-b8"
 # the bf16 configs the >= 70 % of HBM peak target applies to

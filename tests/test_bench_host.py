@@ -35,20 +35,31 @@ def test_cpu_baseline_stops_inside_a_pass_when_the_budget_is_spent():
     assert r["sample"].startswith("fp64 oracle decode of 1 of 4 sequences")
 
 
-@pytest.mark.parametrize("workload,ps,entry", [
-    ("tiny-fp32-decode", 16, "pa_decode_append"),
-    ("qwen2.5-3b-bf16-decode-b64", 256, "pa_decode_append"),
-    ("llama3-8b-bf16-decode-prefix-shared-b256", 256, "pa_decode_cascade"),
-    ("long-context-bf16-splitk-b8", 512, "pa_decode_append"),
-    ("mixed-chunked-prefill-fp8kv", 1024, "pa_decode_append"),
-    ("qwen2.5-3b-bf16-spec-verify-b64", 512, "pa_decode_multi"),
-])
-def test_every_bench_workload_has_measured_traffic_for_the_current_sources(workload, ps, entry):
+BENCH_ENTRY = {
+    "tiny-fp32-decode": "pa_decode_append",
+    "qwen2.5-3b-bf16-decode-b64": "pa_decode_append",
+    "llama3-8b-bf16-decode-prefix-shared-b256": "pa_decode_cascade",
+    "long-context-bf16-splitk-b8": "pa_decode_append",
+    "mixed-chunked-prefill-fp8kv": "pa_decode_append",
+    "qwen2.5-3b-bf16-spec-verify-b64": "pa_decode_multi",
+}
+
+
+def _bench_partition_size(workload):
+    from workloads import CONFIG_NAMES, SPEC_VERIFY_NAME
+    if workload == SPEC_VERIFY_NAME:
+        return bench.SPEC_VERIFY_PS
+    return bench.DEFAULT_PS[{v: k for k, v in CONFIG_NAMES.items()}[workload]]
+
+
+@pytest.mark.parametrize("workload", sorted(BENCH_ENTRY))
+def test_every_bench_workload_has_measured_traffic_for_the_current_sources(workload):
     """profiles/ holds a copy-calibrated FETCH_SIZE + WRITE_SIZE summary for
     each workload at the partition size the bench uses, taken from the
-    decode sources as they stand (a kernel change makes this fail until the
-    counters are taken again)."""
-    t = bench.measured_traffic(workload, ps, entry)
+    decode sources as they stand (a kernel change, or a new bench partition
+    size, makes this fail until the counters are taken again)."""
+    assert sorted(BENCH_ENTRY) == sorted(bench.workload_names())
+    t = bench.measured_traffic(workload, _bench_partition_size(workload), BENCH_ENTRY[workload])
     assert t is not None and t > 0
 
 
@@ -59,6 +70,7 @@ def test_traffic_lookup_refuses_other_partitions_and_entries():
 
 def test_bench_defaults_match_the_summaries():
     assert bench.DEFAULT_PS[5] == 1024 and bench.SPEC_VERIFY_PS == 512 and bench.DEFAULT_PS[1] == 16
+    assert bench.DEFAULT_PS[2] == 512 and bench.DEFAULT_PS[3] == 256 and bench.DEFAULT_PS[4] == 512
     assert os.path.isdir(os.path.join(bench.ROOT, "profiles"))
 
 
