@@ -883,11 +883,16 @@ void decode_kernel(DecodeArgs a) {
                 }
             }
         }
+        // Every lane loads, a column without a query from row 0 (never
+        // written, and no column's arithmetic reads another's): a load taken
+        // by some lanes only is a branch, after which the compiler can no
+        // longer count the loads in flight and waits for all of them -- the
+        // K/V of the tile ahead included -- before the operand is used.
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
             const QT* qrow = reinterpret_cast<const QT*>(a.q) +
                              ((long)max(cs[n], 0) * a.num_heads + chq[n]) * D;
-            Ops::load_q(qd[n], qrow, cs[n] >= 0, lane);
+            Ops::load_q(qd[n], qrow, true, lane);
         }
         cf = a.scale_log2;
         if (KIND == kFP8) cf *= load_invariant(a.k_scale + it.h);
@@ -949,7 +954,10 @@ void decode_kernel(DecodeArgs a) {
     // one that continues it.  A wavefront's LDS writes are performed in
     // order, so once the flag is seen the state is there; the compiler-only
     // fences keep the stores (and, on the taking side, the loads) on their
-    // side of the flag without waiting for the K/V loads in flight.
+    // side of the flag without waiting for the K/V loads in flight.  The
+    // flag is a relaxed workgroup-scope atomic so that it stays an LDS access:
+    // a volatile access through a generic pointer becomes a flat one, which
+    // the compiler follows with a wait on every vector memory load in flight.
     auto park = [&]() __attribute__((always_inline)) {
         SegSlot<NVT, NC>& sl = s_seg[wave];
 #pragma unroll
@@ -961,7 +969,7 @@ void decode_kernel(DecodeArgs a) {
             sl.l[n][lane] = st.l[n];
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) *static_cast<volatile int*>(&s_ready[wave]) = 1;
+        if (lane == 0) __hip_atomic_store(&s_ready[wave], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
     // Take the state of the item cut at g0 from the wavefront holding tile
     // g0 - 1 (the last one before this with a non-empty range; wave 0's range
@@ -975,7 +983,9 @@ void decode_kernel(DecodeArgs a) {
         int from = max(wave - 1, 0);
         while (from > 0 && s_wstart[from] >= g0) --from;
         bool ok = from < wave;
-        for (int spin = 0; ok && *static_cast<volatile int*>(&s_ready[from]) == 0; ++spin) {
+        for (int spin = 0;
+             ok && __hip_atomic_load(&s_ready[from], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+             ++spin) {
             if (spin == (1 << 26)) ok = false;
             __builtin_amdgcn_s_sleep(1);
         }
