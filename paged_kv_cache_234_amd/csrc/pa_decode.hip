@@ -883,11 +883,9 @@ void decode_kernel(DecodeArgs a) {
                 }
             }
         }
-        // Every lane loads, a column without a query from row 0 (never
-        // written, and no column's arithmetic reads another's): a load taken
-        // by some lanes only is a branch, after which the compiler can no
-        // longer count the loads in flight and waits for all of them -- the
-        // K/V of the tile ahead included -- before the operand is used.
+        // Every lane loads, so the loads are no branch of their own: a
+        // column without a query reads row 0 (it is never written, and no
+        // column's arithmetic reads another's).
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
             const QT* qrow = reinterpret_cast<const QT*>(a.q) +
