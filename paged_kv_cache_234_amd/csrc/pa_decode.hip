@@ -1186,8 +1186,13 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // one workgroup of 4 waves per CU and wave slot; fewer for small problems
+    // one workgroup of 4 waves per CU and wave slot; fewer for small problems.
+    // Plain rows use 7/8 of that (the same count on each of the 8 XCDs):
+    // fewer concurrent streams read the pool faster there (Qwen2.5-3B-shaped
+    // batch 30.7 -> 30.3 us in a same-box A/B, long context 377 -> 376 us),
+    // while the wide kernels lose by it.
     long grid = (long)cus * waves_per_simd(KIND, D);
+    if constexpr (PLAIN) grid = grid * 7 / 8;
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
     hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE, CI>), dim3((unsigned)grid), dim3(NW * kWave), 0,
