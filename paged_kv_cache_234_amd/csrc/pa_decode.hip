@@ -492,8 +492,14 @@ void decode_kernel(DecodeArgs a) {
     // X k / NWG, exact: the double product is below 2^53 and a non-integral
     // quotient stays at least 1 / (X k) away from the next integer
     auto share = [&](int x, int k) { return (int)((double)x * k / (double)gridDim.x); };
+    // Range k of the wide kernels goes to a block that runs on the same XCD
+    // as ranges k - 1 and k + 1 (runs of 8; blocks are dealt round-robin to
+    // the XCDs, each with its own L2): a multi-query row's two 32-column
+    // chunks of one partition, neighbours in the tile order, then read their
+    // K/V through one L2 even when a range boundary falls between them.
+    const int kb = PLAIN ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
     if constexpr (!kCost) {
-        const int sa = share(T, blockIdx.x), se = share(T, blockIdx.x + 1);
+        const int sa = share(T, kb), se = share(T, kb + 1);
         if (T > 0) {
             int rsa, rse;
             row_of2(min(sa, T - 1), min(se, T - 1), rsa, rse);
@@ -551,7 +557,7 @@ void decode_kernel(DecodeArgs a) {
             return it.tile0 + it.it_t0 + min(it.o - it.it_c0, it.nti);
         };
         int ca = 0, ce = 0;
-        const int sa = share(C, blockIdx.x), se = share(C, blockIdx.x + 1);
+        const int sa = share(C, kb), se = share(C, kb + 1);
         if (C > 0) {
             int rsa, rse;
             row_of2_in(s_cpre, min(sa, C - 1), min(se, C - 1), rsa, rse);
