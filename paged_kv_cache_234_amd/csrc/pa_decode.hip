@@ -22,10 +22,12 @@
 // Work decomposition.  A work item is (row, virtual head, partition).  Tiles
 // of TT positions are numbered row-major, then virtual head, then position;
 // each workgroup builds the prefix of per-row tile counts in LDS.  With s(g)
-// the item start nearest to tile g, workgroup k takes the whole items whose
+// the item start nearest to tile g, range k holds the whole items whose
 // first tile lies in [s(T k / NWG), s(T (k+1) / NWG)), which is within half
 // an item of an equal share; its NW wavefronts split that run into NW equal
-// runs of tiles.  A wavefront
+// runs of tiles.  Workgroup k takes range k (plain rows) or the range that
+// keeps runs of 8 consecutive ranges on one XCD (group and multi-query rows,
+// whose neighbouring items may read the same K/V).  A wavefront
 // streams its tiles back to back: the next tile's K/V loads -- across item
 // boundaries too -- are in flight while the current tile is multiplied, and a
 // finished item writes its partial (or output) straight from registers.
