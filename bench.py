@@ -133,8 +133,8 @@ class LayerStep:
     """The layer-step the bench times, on device-resident inputs.
 
     step(layer, base) enqueues one layer-step on layer copy `layer % R` of
-    the pool: the append of the step's new tokens (inside the decode launch
-    for plain and prefix-shared decode batches), pa_decode_plan when
+    the pool: the append of the step's new tokens (inside the decode launch,
+    but for the mixed step's chunk tokens), pa_decode_plan when
     plan_due(layer, base), the decode launch, pa_decode_splitk_reduce and,
     for the mixed workload, pa_prefill_chunk.  decode_only(layer) enqueues
     the decode launch alone.  Results land in .out (decode rows, or the
@@ -203,11 +203,17 @@ class LayerStep:
             self.groups = (i32(g_start), i32(g_seqs), i32(g_plens),
                            max(len(m) for m, _ in w.prefix_groups))
         self.has_prefill = w.num_chunks > 0 and not spec
-        # plain and cascade decode steps append each sequence's new token
-        # inside the decode launch (fused: the plain step's pa_decode_append)
-        self.fuse_append = not (spec or self.has_prefill) and fuse_append
-        self.fused = self.fuse_append and not self.cascade
-        if self.fuse_append:
+        # decode steps append each sequence's new token, and the draft step
+        # its draft tokens, inside the decode launch (fused: the plain
+        # step's pa_decode_append)
+        self.fuse_append = not self.has_prefill and fuse_append
+        self.fused = self.fuse_append and not (self.cascade or spec)
+        if self.fuse_append and spec:
+            # the draft tokens, in the query rows' order, are the new tokens
+            if len(w.new_slots) != int(w.query_start_loc[-1]):
+                raise ValueError("a draft step appends its draft tokens only")
+            self.fk, self.fv, self.fslots = self.new_k, self.new_v, self.new_slots
+        elif self.fuse_append:
             rows = np.zeros(B, np.int64)
             fslots = np.full(B, -1, np.int32)
             j = 0
@@ -298,9 +304,11 @@ class LayerStep:
                              pool.v_scale, partition_size=ps, max_partitions=pmax, plan=self.plan,
                              **parts)
         elif self.spec:
+            appended = (dict(k_new=self.fk, v_new=self.fv, new_slots=self.fslots)
+                        if self.fuse_append else {})
             pa_decode_multi(self.q, self.qsl, self.max_q, pool.k, pool.v, self.bt, self.lens,
                             w.scale, ps, pmax, self.part_max, self.part_sum, self.part_out,
-                            pool.k_scale, pool.v_scale, plan=self.plan)
+                            pool.k_scale, pool.v_scale, plan=self.plan, **appended)
         elif self.cascade:
             g_start, g_seqs, g_plens, g_max = self.groups
             appended = (dict(k_new=self.fk, v_new=self.fv, new_slots=self.fslots)
@@ -472,6 +480,8 @@ def run_workload(name, args, dev):
                      % PLAN_LAYERS) if planned else None,
             "step_entries": ("pa_decode_cascade (append fused) + pa_decode_splitk_reduce"
                              if fuse_append and cascade else
+                             "pa_decode_multi (append fused) + pa_decode_splitk_reduce"
+                             if fuse_append and spec else
                              "pa_decode_append + pa_decode_splitk_reduce" if fused and ps > 0
                              else "pa_decode_append" if fused
                              else "pa_kv_append + %s%s%s" % (

@@ -210,10 +210,11 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
  *               the cascade).  The workgroup count depends on the device's
  *               compute units.
  *   entry       the decode entry point that will use the plan
- *   new_slots   NULL, or the new_slots the launches will append with (append
- *               and cascade entries): the plan then lists, per wavefront,
- *               the tokens it writes (checked against the tables once), so
- *               the launch loads all their rows at once
+ *   new_slots   NULL, or the new_slots the launches will append with: the
+ *               plan then lists, per wavefront, the tokens it writes (checked
+ *               against the tables once; a wavefront with more than 8 finds
+ *               them again in the launch), so the launch loads all their
+ *               rows at once
  *   group_*, num_groups, max_group_size   the cascade's groups (else NULL, 0)
  *   query_start_loc, max_query_len        pa_decode_multi's query map (else
  *                                         NULL, 0)
@@ -293,7 +294,8 @@ pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
  * multi-token-prediction draft tokens).  Sequence b's q_b = query_start_loc[b+1] - query_start_loc[b]
  * tokens are rows query_start_loc[b] .. +q_b-1 of q, at positions
  * L_b - q_b .. L_b - 1; the token at position P sees positions 0 .. P.
- * Their K/V must already be appended.  Each (K/V tile, KV head) is read once
+ * Their K/V are appended beforehand or by this launch (below).  Each
+ * (K/V tile, KV head) is read once
  * for up to 16 / G of a sequence's query tokens.
  *   q                  [query_start_loc[batch]][num_heads][head_dim]
  *   part_*             [query_start_loc[batch]][num_heads][max_partitions]
@@ -307,11 +309,24 @@ pa_status_t pa_decode_cascade(const void* q, pa_dtype_t q_dtype,
  *                      longer chunks are prefill: pa_prefill_chunk)
  * Requires partition_size > 0 and q_b <= L_b.
  */
-/* plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_MULTI
+/* k_new, v_new, new_slots: NULL, or the query tokens' own K/V appended in
+ * the same launch, with the pool bytes and results of pa_kv_append of
+ * them followed by this call (all three NULL: no append).
+ *   k_new, v_new   [query_start_loc[batch]][num_kv_heads][head_dim] of
+ *                  q_dtype, rows as q's
+ *   new_slots      [query_start_loc[batch]] int32: the token's slot, which
+ *                  must be its position's slot in b's block table, or -1
+ *                  when its K/V are already in the pool; any other value
+ *                  writes nothing
+ * Every wavefront that reads a tile holding one of b's query positions for
+ * KV head h writes b's query tokens for h first (the same bytes whichever
+ * writes them), so no other launch or synchronisation is needed.
+ * plan, plan_bytes: NULL / 0, or a plan made with PA_PLAN_DECODE_MULTI
  * (see pa_decode_plan). */
 pa_status_t pa_decode_multi(const void* q, pa_dtype_t q_dtype,
+                            const void* k_new, const void* v_new, const int32_t* new_slots,
                             const int32_t* query_start_loc, int32_t max_query_len,
-                            const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype,
+                            void* k_cache, void* v_cache, pa_dtype_t cache_dtype,
                             const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t batch,

@@ -59,9 +59,9 @@ def load(path=LIB_PATH):
                                       vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
                                       ctypes.c_size_t, st]
-    lib.pa_decode_multi.argtypes = [vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32,
-                                    i32, i32, i32, f32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t,
-                                    st]
+    lib.pa_decode_multi.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp, i32,
+                                    vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp, vp,
+                                    ctypes.c_size_t, st]
     lib.pa_decode_splitk_reduce.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, st]
     lib.pa_prefill_chunk.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, vp, i32, vp,
                                      i32, i32, i32, i32, f32, st]
@@ -364,9 +364,12 @@ def pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, scale, gr
 
 def pa_decode_multi(q, query_start_loc, max_query_len, k_cache, v_cache, block_tables,
                     context_lens, scale, partition_size, max_partitions, part_max, part_sum,
-                    part_out, k_scale=None, v_scale=None, plan=None, stream=None):
+                    part_out, k_scale=None, v_scale=None, plan=None, k_new=None, v_new=None,
+                    new_slots=None, stream=None):
     """Split-K partials for q_b causal query tokens per sequence: q [T, Hq, D]
-    with T = query_start_loc[-1]; partials [T, Hq, max_partitions] (+ [D])."""
+    with T = query_start_loc[-1]; partials [T, Hq, max_partitions] (+ [D]).
+    k_new, v_new [T, Hkv, D] and new_slots int32 [T] (-1 to skip): the query
+    tokens' K/V, appended in the same launch (all three None: no append)."""
     nb, hkv, bs, d = _pool_dims(k_cache, v_cache)
     T, hq = q.shape[0], q.shape[1]
     B = context_lens.numel()
@@ -380,7 +383,16 @@ def pa_decode_multi(q, query_start_loc, max_query_len, k_cache, v_cache, block_t
             raise ValueError("part_max/part_sum must be float32 %s" % (want,))
     if part_out is None or tuple(part_out.shape) != want + (d,):
         raise ValueError("part_out must be float32 %s" % (want + (d,),))
-    st = load().pa_decode_multi(_ptr(q), _dt(q), _i32(query_start_loc, "query_start_loc"),
+    if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots is None):
+        raise ValueError("k_new, v_new and new_slots go together")
+    if k_new is not None and (tuple(k_new.shape) != (T, hkv, d) or k_new.dtype != q.dtype
+                              or tuple(v_new.shape) != (T, hkv, d) or v_new.dtype != q.dtype
+                              or new_slots.numel() != T):
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim] of q's dtype and "
+                         "new_slots one entry per query token")
+    st = load().pa_decode_multi(_ptr(q), _dt(q), _ptr(k_new), _ptr(v_new),
+                                None if new_slots is None else _i32(new_slots, "new_slots"),
+                                _i32(query_start_loc, "query_start_loc"),
                                 int(max_query_len), _ptr(k_cache), _ptr(v_cache), _dt(k_cache),
                                 _ptr(k_scale), _ptr(v_scale), _i32(block_tables, "block_tables"),
                                 block_tables.shape[1], _i32(context_lens, "context_lens"), B, hq,

@@ -143,6 +143,11 @@ template <int NVT, int NC> struct SegSlot {
 // partial write and the cursor's turn), so many short items weigh like the
 // long ones they stand beside.
 constexpr int kWideItemCost = 1;
+// A plan whose launches append also charges kAppendCost to the last item of
+// each virtual head of a row with a token to append: the wavefront that
+// holds it waits for the token's rows before its second tile's loads go out,
+// so it takes a little less other work.
+constexpr int kAppendCost = 1;
 
 // NC: 16-column query tiles per wavefront.  Sequence rows use one (their
 // columns are one KV head's G <= 16 query heads); group and multi-query rows
@@ -305,6 +310,13 @@ void decode_kernel(DecodeArgs a) {
         const int last = row_skip(r) + n - 1;
         return (n - 1) * tpi + (s_len[r] - last * PS + TT - 1) / TT;
     };
+    // extra cost of the last item of each virtual head of row r (plans whose
+    // launches append: sequence rows with a position, multi-query rows with
+    // a query token)
+    auto append_cost = [&](int r) {
+        if (!kCost || a.new_slots == nullptr || r >= B || row_items(r) == 0) return 0;
+        return (multi ? (s_aux[r] & 0xFF) > 0 : s_len[r] > 0) ? kAppendCost : 0;
+    };
     // plain decode keeps it in s_aux (otherwise unused) once the prefix is built
     auto row_head_tiles = [&](int r) { return PLAIN ? s_aux[r] : head_tiles_of(r); };
     // Tile order within a row.  Sequence and group rows: virtual head (KV
@@ -399,7 +411,9 @@ void decode_kernel(DecodeArgs a) {
     // ---- prefix of per-row tile counts (each thread: a run of rows) ---------
     const int per = (R + NT - 1) / NT;
     const int r0 = tid * per;
-    auto row_cost = [&](int r) { return row_heads(r) * (head_tiles_of(r) + kItemCost * row_items(r)); };
+    auto row_cost = [&](int r) {
+        return row_heads(r) * (head_tiles_of(r) + kItemCost * row_items(r) + append_cost(r));
+    };
     int local = 0, local_c = 0;
     for (int k = 0; k < per; ++k)
         if (r0 + k < R) {
@@ -520,14 +534,14 @@ void decode_kernel(DecodeArgs a) {
         // head's first tile and cost, the offset o of c in the head, and the
         // item's first tile, first cost and tiles relative to the head
         struct ItemAt {
-            int tile0, cost0, o, it_t0, it_c0, nti;
+            int tile0, cost0, o, it_t0, it_c0, nti, ic;
         };
         auto item_at_cost = [&](int c, int r) {
             ItemAt it;
-            const int th = head_tiles_of(r), n = row_items(r);
+            const int th = head_tiles_of(r), n = row_items(r), ea = append_cost(r);
             const int nch = CI ? row_heads(r) / Hkv : 1;      // (otherwise each virtual head is a unit)
             const int rem = th - (n - 1) * tpi;
-            const int chead = nch * (th + kItemCost * n);         // cost of one KV head
+            const int chead = nch * (th + kItemCost * n + ea);    // cost of one KV head
             const int h = (c - s_cpre[r]) / chead;
             it.tile0 = s_tpre[r] + h * nch * th;
             it.cost0 = s_cpre[r] + h * chead;
@@ -538,18 +552,20 @@ void decode_kernel(DecodeArgs a) {
                 it.it_c0 = k * ci;
                 it.it_t0 = k * tpi;
                 it.nti = tpi;
+                it.ic = ci;
             } else {
-                const int cr = rem + kItemCost;
+                const int cr = rem + kItemCost + ea;
                 const int j = min((it.o - full_c) / cr, nch - 1);
                 it.it_c0 = full_c + j * cr;
                 it.it_t0 = (n - 1) * nch * tpi + j * rem;
                 it.nti = rem;
+                it.ic = cr;
             }
             return it;
         };
         auto nearest_item_by_cost = [&](int c, int r, int& tile, int& cost) {
             const ItemAt it = item_at_cost(c, r);
-            const int before = it.it_c0, after = it.it_c0 + it.nti + kItemCost;
+            const int before = it.it_c0, after = it.it_c0 + it.ic;
             const bool take_before = it.o - before <= after - it.o;
             tile = it.tile0 + it.it_t0 + (take_before ? 0 : it.nti);
             cost = it.cost0 + (take_before ? before : after);
@@ -600,13 +616,53 @@ void decode_kernel(DecodeArgs a) {
     // b's new token for head h there before loading anything.  A wavefront's
     // vector memory accesses to one address are performed in order, so its
     // later K/V loads of that block return the new token without a wait.
-    // (sequence rows only: plain decode and the cascade's member rows)
+    // A multi-query row's q tokens, at positions L - q .. L - 1, may span
+    // tiles and are read by the wavefronts of both chunks of query columns:
+    // every wavefront that loads a tile of KV head h holding one of those
+    // positions writes all q tokens of head h first (the same bytes
+    // whichever wavefront writes them, so the others' stores change nothing
+    // it reads).
     constexpr int IB = KIND == kF32 ? 4 : 2;              // input element bytes
-    // f(r, h, slot) for each token this wavefront writes, in order
+    // multi-query row r: whether tiles g0 .. g1 - 1 hold a tile of KV head h
+    // with one of its query positions.  Partitions p start at multiples of
+    // PS and their tiles jj at multiples of TT within them; the tile number
+    // follows the multi-query order (KV head, partition, chunk).
+    auto multi_holds = [&](int r, int h) {
+        const int th = row_head_tiles(r), base = s_tpre[r];
+        const int L = s_len[r], x0 = L - (s_aux[r] & 0xFF);
+        const int nch = row_heads(r) / Hkv, n = row_items(r);
+        const int rem = th - (n - 1) * tpi, hb = nch * th, full = (n - 1) * nch * tpi;
+        for (int p = x0 / PS; p <= (L - 1) / PS; ++p) {
+            const int pb = p * PS;
+            const int j_lo = (max(x0, pb) - pb) / TT, j_hi = (min(L, pb + PS) - 1 - pb) / TT;
+            for (int ch = 0; ch < nch; ++ch) {
+                const int t0 = base + h * hb + (p < n - 1 ? p * nch * tpi + ch * tpi : full + ch * rem);
+                if (t0 + j_lo < g1 && t0 + j_hi >= g0) return true;
+            }
+        }
+        return false;
+    };
+    // f(t, h, slot) for each token this wavefront writes, in order; t is the
+    // token's row of k_new / v_new (the sequence for one new token per
+    // sequence, the query token for multi-query rows)
     auto for_each_append = [&](auto&& f) {
         for (int r = rg0; r <= min(rg1, B - 1); ++r) {
             const int th = row_head_tiles(r);
             if (th == 0) continue;
+            if (multi) {
+                const int nq = s_aux[r] & 0xFF, q0 = s_aux[r] >> 8, x0 = s_len[r] - nq;
+                for (int h = 0; h < Hkv && nq > 0; ++h) {
+                    if (!multi_holds(r, h)) continue;
+                    for (int i = 0; i < nq; ++i) {
+                        const int pos = x0 + i;
+                        const int slot = load_invariant(a.new_slots + q0 + i);
+                        const int want = load_invariant(a.block_tables + (long)r * a.max_blocks_per_seq +
+                                                        pos / kBlock) * kBlock + pos % kBlock;
+                        if (slot >= 0 && slot == want) f(q0 + i, h, slot);
+                    }
+                }
+                continue;
+            }
             const int base = s_tpre[r];
             // first head whose last tile, base + (h + 1) * th - 1, is at or after g0
             const int x = g0 - base + 1;
@@ -631,9 +687,37 @@ void decode_kernel(DecodeArgs a) {
     // (a plan's list of tokens is written where the first tile is loaded)
     const bool listed_appends = MODE == kUsePlan && a.new_slots != nullptr && plan_apps >= 0;
     if (MODE != kMakePlan && a.new_slots != nullptr && ntiles > 0) {
-        if (!listed_appends) {
-            for_each_append([&](int r, int h, int slot) {
-                const long row = ((long)r * Hkv + h) * D * IB;
+        if (!listed_appends && multi) {
+            // a row's tokens 512 / D at a time, D / 8 lanes each: one memory
+            // round trip per group rather than two per token
+            constexpr int CPT = D / 8, TPP = kWave / CPT;
+            for (int r = rg0; r <= min(rg1, B - 1); ++r) {
+                const int nq = s_aux[r] & 0xFF, q0 = s_aux[r] >> 8, x0 = s_len[r] - nq;
+                if (nq <= 0 || row_head_tiles(r) == 0) continue;
+                const int32_t* brow = a.block_tables + (long)r * a.max_blocks_per_seq;
+                for (int h = 0; h < Hkv; ++h) {
+                    if (!multi_holds(r, h)) continue;
+                    float ksc, vsc;
+                    scales(h, ksc, vsc);
+                    for (int i0 = 0; i0 < nq; i0 += TPP) {
+                        const int i = i0 + lane / CPT;
+                        if (i >= nq) continue;
+                        const int pos = x0 + i;
+                        const int slot = a.new_slots[q0 + i];
+                        const int want = brow[pos / kBlock] * kBlock + pos % kBlock;
+                        const long row = ((long)(q0 + i) * Hkv + h) * D * IB;
+                        const TokenChunk<KIND> tok = load_token_chunk<KIND, D>(
+                            static_cast<const char*>(a.k_new) + row,
+                            static_cast<const char*>(a.v_new) + row, lane % CPT);
+                        if (slot >= 0 && slot == want)
+                            store_token_chunk<KIND, D>(tok, a.k_cache_w, a.v_cache_w, slot / kBlock,
+                                                       slot % kBlock, h, Hkv, lane % CPT, ksc, vsc);
+                    }
+                }
+            }
+        } else if (!listed_appends) {
+            for_each_append([&](int t, int h, int slot) {
+                const long row = ((long)t * Hkv + h) * D * IB;
                 float ksc, vsc;
                 scales(h, ksc, vsc);
                 if (lane < D / 8)
@@ -807,9 +891,9 @@ void decode_kernel(DecodeArgs a) {
         // the tokens this wavefront appends, checked against the tables now
         int napp = 0;
         if (a.new_slots != nullptr && ntiles > 0)
-            for_each_append([&](int r, int h, int slot) {
+            for_each_append([&](int t, int h, int slot) {
                 if (napp < kPlanMaxAppends) {
-                    if (lane == 16 + 2 * napp) w = r * Hkv + h;
+                    if (lane == 16 + 2 * napp) w = t * Hkv + h;
                     if (lane == 17 + 2 * napp) w = slot;
                 }
                 ++napp;
@@ -1027,7 +1111,8 @@ void decode_kernel(DecodeArgs a) {
         // carry one token, so a register set holds 512 / D): their rows are
         // loaded before anything else.  The stores must precede the loads of
         // the tile holding the token (the last tile of a listed (row, KV
-        // head)), which then reads it back.  The plain kernel issues them just
+        // head), or the first tile holding a query position of a
+        // multi-query row), which then reads it back.  The plain kernel issues them just
         // before that tile's loads -- usually tiles later, when the rows have
         // long arrived, so the stream never waits for them.  The wide kernels
         // have no registers to hold the rows that long: they store as soon as
@@ -1073,8 +1158,13 @@ void decode_kernel(DecodeArgs a) {
             }
             stored = true;
         };
-        // the tile under cursor c holds a listed token not stored yet
+        // the tile under cursor c holds a listed token not stored yet (a
+        // multi-query row's tokens may span tiles: any tile holding one of
+        // its query positions is taken to hold them all; a token is listed
+        // only for a wavefront that loads such a tile, so the first of them
+        // comes no later than the token's own)
         auto holds_token = [&](const Cursor& c) __attribute__((always_inline)) {
+            if (multi) return !stored && c.tb + (c.jj + 1) * TT > c.qmin;
             if (stored || c.p + 1 != c.n || c.jj + 1 != c.nti) return false;
             bool hit = false;
 #pragma unroll
@@ -1442,8 +1532,9 @@ extern "C" pa_status_t pa_decode_cascade(
 }
 
 extern "C" pa_status_t pa_decode_multi(
-    const void* q, pa_dtype_t q_dtype, const int32_t* query_start_loc, int32_t max_query_len,
-    const void* k_cache, const void* v_cache, pa_dtype_t cache_dtype, const float* k_scale,
+    const void* q, pa_dtype_t q_dtype, const void* k_new, const void* v_new,
+    const int32_t* new_slots, const int32_t* query_start_loc, int32_t max_query_len,
+    void* k_cache, void* v_cache, pa_dtype_t cache_dtype, const float* k_scale,
     const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t batch, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, float scale, int32_t partition_size,
@@ -1463,6 +1554,8 @@ extern "C" pa_status_t pa_decode_multi(
     bool none = false;
     st = set_multi(a, query_start_loc, max_query_len, items, none);
     if (st != PA_OK || none) return st;
+    st = set_append(a, k_new, v_new, new_slots, k_cache, v_cache);
+    if (st != PA_OK) return st;
     if (plan) {
         if (!plan_fits(plan_bytes, batch, cache_dtype, head_dim)) return PA_ERR_ARG;
         a.plan = plan;
@@ -1533,7 +1626,7 @@ extern "C" pa_status_t pa_decode_plan(int32_t* plan, size_t plan_bytes, pa_plan_
     }
     if (st != PA_OK) return st;
     if (!plan_fits(plan_bytes, rows, cache_dtype, head_dim)) return PA_ERR_ARG;
-    if (entry != PA_PLAN_DECODE_MULTI) a.new_slots = new_slots;
+    a.new_slots = new_slots;
     a.plan_out = plan;
     return run_decode(a, cache_dtype, head_dim, items, entry != PA_PLAN_DECODE_APPEND, stream);
 }

@@ -184,9 +184,20 @@ def token_lens(w):
     return np.asarray(out, np.int64)
 
 
-def run_multi(w, pool, partition_size, device="cuda", planned=False):
+def chunk_new_tokens(w, device="cuda"):
+    """The chunks' query tokens, in q_prefill's row order: K/V [T, Hkv, D]
+    and their slots [T] (the last T entries of the step's new tokens)."""
+    T = int(w.query_start_loc[-1])
+    rows, slots = w.new_rows[len(w.new_rows) - T:], w.new_slots[len(w.new_slots) - T:]
+    idx = torch.as_tensor(rows, device=w.fill_k.device)
+    return (w.fill_k[idx].to(device).contiguous(), w.fill_v[idx].to(device).contiguous(),
+            i32(slots, device))
+
+
+def run_multi(w, pool, partition_size, device="cuda", planned=False, appended=None):
     """pa_decode_multi over the workload's chunks (optionally through a
-    launch plan) + pa_decode_splitk_reduce over their rows; returns (out,
+    launch plan, optionally appending (k_new, v_new, new_slots) in the same
+    launch) + pa_decode_splitk_reduce over their rows; returns (out,
     (pm, ps, po), token_lens)."""
     qp = w.q_prefill.to(device).contiguous()
     T, hq, d = qp.shape
@@ -203,9 +214,10 @@ def run_multi(w, pool, partition_size, device="cuda", planned=False):
     if planned:
         plan = decode_plan_buffer(w.num_chunks, pool.k, d, device)
         pa_decode_plan(plan, cbt, clens, w.num_heads, pool.k, pool.v, partition_size, pmax,
-                       queries=(qslt, maxq))
+                       queries=(qslt, maxq), new_slots=appended[2] if appended else None)
+    kw = dict(zip(("k_new", "v_new", "new_slots"), appended)) if appended else {}
     pa_decode_multi(qp, qslt, maxq, pool.k, pool.v, cbt, clens, w.scale, partition_size, pmax, pm,
-                    ps, po, pool.k_scale, pool.v_scale, plan=plan)
+                    ps, po, pool.k_scale, pool.v_scale, plan=plan, **kw)
     out = torch.empty_like(qp)
     pa_decode_splitk_reduce(out, pm, ps, po, i32(tl, device), partition_size)
     return out, (pm, ps, po), tl

@@ -122,12 +122,15 @@ def test_cascade_validation():
 def test_multi_query_validation():
     lib = _lib.load()
 
-    def call(ps=64, pmax=4, B=4, mq=8, qsl=FAKE, parts=FAKE, plan=None, nbytes=0):
-        return lib.pa_decode_multi(FAKE, 1, qsl, mq, FAKE, FAKE, 1, None, None, FAKE, 32, FAKE, B,
-                                   8, 2, 128, 16, 0.1, ps, pmax, parts, parts, parts, plan,
-                                   nbytes, None)
+    def call(ps=64, pmax=4, B=4, mq=8, qsl=FAKE, parts=FAKE, plan=None, nbytes=0,
+             new=(None, None, None)):
+        return lib.pa_decode_multi(FAKE, 1, *new, qsl, mq, FAKE, FAKE, 1, None, None, FAKE, 32,
+                                   FAKE, B, 8, 2, 128, 16, 0.1, ps, pmax, parts, parts, parts,
+                                   plan, nbytes, None)
 
     assert call(ps=0) == _lib.PA_ERR_ARG
+    assert call(new=(FAKE, None, FAKE)) == _lib.PA_ERR_ARG       # append arrays: all or none
+    assert call(new=(None, None, FAKE)) == _lib.PA_ERR_ARG
     assert call(parts=None) == _lib.PA_ERR_ARG
     assert call(qsl=None) == _lib.PA_ERR_ARG
     assert call(mq=-1) == _lib.PA_ERR_ARG

@@ -8,7 +8,9 @@ oracle's partitions for a context of that token's position + 1.  Cases cover
 one to 64 query tokens (one and several 16-column chunks per KV head), a
 prefix of zero, contexts that end on and off tile and partition boundaries,
 every GQA regime (16 / G query tokens per 16 MFMA columns) and all three cache
-types on NaN-poisoned pools.
+types on NaN-poisoned pools.  The query tokens' K/V appended by the launch
+itself give the pool bytes, outputs and partials of pa_kv_append followed by
+pa_decode_multi, bit for bit.
 """
 
 import numpy as np
@@ -16,8 +18,9 @@ import pytest
 import torch
 
 from oracle import paged_attention as opa
-from tests.gpu_helpers import (TOL, as_f64, gpu_pool, host, max_abs_err, oracle_pool, run_decode,
-                               run_multi, token_lens)
+from paged_kv_cache_234_amd import pa_kv_append
+from tests.gpu_helpers import (TOL, as_f64, chunk_new_tokens, gpu_pool, host, max_abs_err,
+                               oracle_pool, run_decode, run_multi)
 from workloads import build_workload, make_spec_verify
 
 pytestmark = pytest.mark.gpu
@@ -146,3 +149,87 @@ def test_planned_equals_unplanned_bit_exact(cache):
     assert torch.equal(a_out, b_out)
     for x, y in zip(a_parts, b_parts):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+# drafts that cross 16-token blocks (14 + 2, 15 + 8, 62 + 4, 127 + 8, 255 + 6)
+# and, at partition sizes 16 and 32, partitions
+def _fused_equals_separate(w, ps, planned):
+    """The query tokens appended by the multi-query launch itself against
+    pa_kv_append then pa_decode_multi, both on pools that lack them: the same
+    pool bytes, and outputs and partials bit for bit."""
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    k_new, v_new, s = chunk_new_tokens(w)
+    pa_kv_append(k_new, v_new, pool_a.k, pool_a.v, s, pool_a.k_scale, pool_a.v_scale)
+    out_a, parts_a, _ = run_multi(w, pool_a, ps, planned=planned)
+    out_b, parts_b, _ = run_multi(w, pool_b, ps, planned=planned, appended=(k_new, v_new, s))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
+    assert torch.equal(out_a.view(torch.uint8), out_b.view(torch.uint8))
+    for x, y in zip(parts_a, parts_b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    return out_b
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+@pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_fused_append_equals_append_then_multi(cache, planned, ps):
+    w = _case(cache, 16, 2, 128, CHUNKS, seed=ps + 5)
+    out = _fused_equals_separate(w, ps, planned)
+    kp, vp = oracle_pool(w)
+    ref = opa.oracle_prefill(host(w.q_prefill), w.q_dtype, w.query_start_loc, kp, vp,
+                             w.cache_dtype, w.chunk_block_tables, w.chunk_context_lens, w.scale,
+                             w.k_scale, w.v_scale, w.block_size)
+    assert max_abs_err(as_f64(out), ref) <= TOL[cache]
+
+
+@pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 64), (12, 4, 128), (32, 8, 128), (16, 1, 64)])
+def test_fused_append_all_group_sizes(hq, hkv, d, planned):
+    _fused_equals_separate(_case("bf16", hq, hkv, d, CHUNKS, seed=hq + hkv), 32, planned)
+
+
+@pytest.mark.parametrize("planned", [False, True])
+def test_fused_append_more_than_eight_tokens_per_wavefront(planned):
+    """Drafts of up to 64 tokens: every wavefront that holds one has more
+    tokens to write than a plan lists, so a planned launch finds them in
+    the tables again."""
+    w = _case("bf16", 32, 8, 128, [(0, 64), (5, 64), (300, 33), (64, 17), (9, 2)], seed=78)
+    _fused_equals_separate(w, 64, planned)
+
+
+@pytest.mark.parametrize("planned", [False, True])
+def test_fused_append_rows_without_queries(planned):
+    w = _case("fp8", 16, 2, 128, [(40, 0), (15, 8), (0, 0), (100, 3), (33, 0)], seed=12)
+    _fused_equals_separate(w, 32, planned)
+
+
+@pytest.mark.parametrize("planned", [False, True])
+def test_fused_append_writes_no_skipped_or_off_table_slot(planned):
+    """Slot -1 and a slot other than the table's for the token's position
+    write nothing: on a pool that already holds every token, its bytes and
+    the results are those of the launch without an append."""
+    w = _case("bf16", 16, 2, 128, CHUNKS, seed=19)
+    pool = gpu_pool(w)
+    want, _, _ = run_multi(w, pool, 64, planned=planned)
+    torch.cuda.synchronize()
+    before_k, before_v = pool.k.clone(), pool.v.clone()
+    k_new, v_new, slots = chunk_new_tokens(w)
+    bad = slots.clone()
+    bad[0::2] = -1
+    bad[1::2] += 1                          # the next slot: not the token's position
+    # garbage rows: nothing may be written from them
+    k_bad, v_bad = torch.full_like(k_new, float("nan")), torch.full_like(v_new, float("nan"))
+    got, _, _ = run_multi(w, pool, 64, planned=planned, appended=(k_bad, v_bad, bad))
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k.view(torch.uint8), before_k.view(torch.uint8))
+    assert torch.equal(pool.v.view(torch.uint8), before_v.view(torch.uint8))
+    assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("planned", [False, True])
+def test_fused_append_spec_verify_full_size(planned):
+    """The draft-verification workload at full size and the bench's
+    partition size."""
+    _fused_equals_separate(make_spec_verify(device="cuda"), 512, planned)
