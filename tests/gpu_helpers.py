@@ -194,11 +194,13 @@ def chunk_new_tokens(w, device="cuda"):
             i32(slots, device))
 
 
-def run_multi(w, pool, partition_size, device="cuda", planned=False, appended=None):
+def run_multi(w, pool, partition_size, device="cuda", planned=False, appended=None,
+              plan_lists=True):
     """pa_decode_multi over the workload's chunks (optionally through a
     launch plan, optionally appending (k_new, v_new, new_slots) in the same
-    launch) + pa_decode_splitk_reduce over their rows; returns (out,
-    (pm, ps, po), token_lens)."""
+    launch; plan_lists: the plan is made with those new_slots) +
+    pa_decode_splitk_reduce over their rows; returns (out, (pm, ps, po),
+    token_lens)."""
     qp = w.q_prefill.to(device).contiguous()
     T, hq, d = qp.shape
     qsl = w.query_start_loc
@@ -214,7 +216,8 @@ def run_multi(w, pool, partition_size, device="cuda", planned=False, appended=No
     if planned:
         plan = decode_plan_buffer(w.num_chunks, pool.k, d, device)
         pa_decode_plan(plan, cbt, clens, w.num_heads, pool.k, pool.v, partition_size, pmax,
-                       queries=(qslt, maxq), new_slots=appended[2] if appended else None)
+                       queries=(qslt, maxq),
+                       new_slots=appended[2] if appended and plan_lists else None)
     kw = dict(zip(("k_new", "v_new", "new_slots"), appended)) if appended else {}
     pa_decode_multi(qp, qslt, maxq, pool.k, pool.v, cbt, clens, w.scale, partition_size, pmax, pm,
                     ps, po, pool.k_scale, pool.v_scale, plan=plan, **kw)

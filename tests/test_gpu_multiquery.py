@@ -153,15 +153,18 @@ def test_planned_equals_unplanned_bit_exact(cache):
 
 # drafts that cross 16-token blocks (14 + 2, 15 + 8, 62 + 4, 127 + 8, 255 + 6)
 # and, at partition sizes 16 and 32, partitions
-def _fused_equals_separate(w, ps, planned):
+def _fused_equals_separate(w, ps, planned, plan_lists=True):
     """The query tokens appended by the multi-query launch itself against
     pa_kv_append then pa_decode_multi, both on pools that lack them: the same
-    pool bytes, and outputs and partials bit for bit."""
+    pool bytes, and outputs and partials bit for bit.  plan_lists=False: the
+    plan is made without new_slots (the launch then finds every token
+    itself)."""
     pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
     k_new, v_new, s = chunk_new_tokens(w)
     pa_kv_append(k_new, v_new, pool_a.k, pool_a.v, s, pool_a.k_scale, pool_a.v_scale)
     out_a, parts_a, _ = run_multi(w, pool_a, ps, planned=planned)
-    out_b, parts_b, _ = run_multi(w, pool_b, ps, planned=planned, appended=(k_new, v_new, s))
+    out_b, parts_b, _ = run_multi(w, pool_b, ps, planned=planned, appended=(k_new, v_new, s),
+                                  plan_lists=plan_lists)
     torch.cuda.synchronize()
     assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
     assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
@@ -197,6 +200,12 @@ def test_fused_append_more_than_eight_tokens_per_wavefront(planned):
     the tables again."""
     w = _case("bf16", 32, 8, 128, [(0, 64), (5, 64), (300, 33), (64, 17), (9, 2)], seed=78)
     _fused_equals_separate(w, 64, planned)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_fused_append_through_a_plan_that_lists_no_tokens(cache):
+    w = _case(cache, 16, 2, 128, CHUNKS, seed=23)
+    _fused_equals_separate(w, 32, True, plan_lists=False)
 
 
 @pytest.mark.parametrize("planned", [False, True])
