@@ -613,7 +613,8 @@ void decode_kernel(DecodeArgs a) {
 
     // ---- fused append: the wavefront holding the last tile of (b, h) -- the
     // only one that reads the block of position L_b - 1 for head h -- writes
-    // b's new token for head h there before loading anything.  A wavefront's
+    // b's new token for head h there before it loads that tile (unplanned
+    // launches: before loading anything; planned ones: below).  A wavefront's
     // vector memory accesses to one address are performed in order, so its
     // later K/V loads of that block return the new token without a wait.
     // A multi-query row's q tokens, at positions L - q .. L - 1, may span
