@@ -194,6 +194,13 @@ def test_fused_append_all_group_sizes(hq, hkv, d, planned):
 
 
 @pytest.mark.parametrize("planned", [False, True])
+@pytest.mark.parametrize("cache", ["f32", "fp8"])
+def test_fused_append_head_dim_64(cache, planned):
+    """head_dim 64: 8 lanes per token row, 8 rows per wave-wide pass."""
+    _fused_equals_separate(_case(cache, 8, 2, 64, CHUNKS, seed=64), 32, planned)
+
+
+@pytest.mark.parametrize("planned", [False, True])
 def test_fused_append_more_than_eight_tokens_per_wavefront(planned):
     """Drafts of up to 64 tokens: every wavefront that holds one has more
     tokens to write than a plan lists, so a planned launch finds them in
