@@ -221,7 +221,8 @@ pa_status_t pa_decode_append(void* out, const void* q, pa_dtype_t q_dtype,
  *   other arguments as that entry point (Q, K/V and scales are not read)
  * Plans for prefix-group and multi-query rows also balance cost rather than
  * tiles across workgroups: an item counts one extra tile, for its Q load and
- * its partial write, so many short items weigh like a few long ones.
+ * its partial write, so many short items weigh like a few long ones, and one
+ * more when it ends a (virtual) head whose token the launch appends.
  * The plan stays valid while context_lens, the first ceil(L_b / 16)
  * block-table entries of every row, new_slots, and the groups or query map
  * are unchanged.  It follows the stream: the plan launch must precede its users
