@@ -249,3 +249,20 @@ def test_fused_append_spec_verify_full_size(planned):
     """The draft-verification workload at full size and the bench's
     partition size."""
     _fused_equals_separate(make_spec_verify(device="cuda"), 512, planned)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_append_seeded_random_configurations(seed):
+    """Seeded random shapes: cache type, head size, GQA shape, partition
+    size (a multiple of 16 up to 512), 1-12 sequences of 1-64 query tokens
+    over prefixes of 0-2000 positions, planned or not."""
+    rng = np.random.default_rng(1000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8)][int(rng.integers(6))]
+    d = [64, 128][int(rng.integers(2))]
+    n = int(rng.integers(1, 13))
+    chunks = [(int(rng.integers(0, 2001)), int(rng.integers(1, 65))) for _ in range(n)]
+    ps = 16 * int(rng.integers(1, 33))
+    print("fused multi append:", seed, cache, hq, hkv, d, ps, chunks, flush=True)
+    _fused_equals_separate(_case(cache, hq, hkv, d, chunks, seed=seed), ps,
+                           bool(rng.integers(2)))
