@@ -179,3 +179,53 @@ def test_cascade_fused_append_equals_append_then_cascade(cache, planned):
     assert torch.equal(got, want)
     for a, b in zip(parts_a, parts_b):
         assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
+
+
+def _random_groups(rng, B):
+    """1-4 groups of 2-8 consecutive members sharing 1-12 blocks (members'
+    lengths at least the shared prefix; about a quarter end on it, so their
+    newest token sits in a shared block), with gaps of sequences in no
+    group."""
+    lens = [int(x) for x in rng.integers(0, 2001, size=B)]
+    groups, b = [], 0
+    for _ in range(int(rng.integers(1, 5))):
+        size, nshared = int(rng.integers(2, 9)), int(rng.integers(1, 13))
+        if b + size > B:
+            break
+        members = list(range(b, b + size))
+        for m in members:
+            lens[m] = 16 * nshared + (0 if int(rng.integers(4)) == 0 else int(rng.integers(1, 1001)))
+        groups.append((members, nshared))
+        b += size + int(rng.integers(0, 3))
+    return lens, groups
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cascade_fused_append_seeded_random_configurations(seed):
+    """Seeded random prefix groups, shapes and partition sizes (multiples of
+    16 up to 512): the cascade launch that appends each member's newest
+    token equals pa_kv_append followed by pa_decode_cascade, bit for bit,
+    planned or not."""
+    from paged_kv_cache_234_amd import pa_kv_append
+    from tests.gpu_helpers import decode_new_tokens
+    rng = np.random.default_rng(3000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8)][int(rng.integers(6))]
+    d = [64, 128][int(rng.integers(2))]
+    lens, groups = _random_groups(rng, int(rng.integers(8, 41)))
+    ps = 16 * int(rng.integers(1, 33))
+    planned = bool(rng.integers(2))
+    print("cascade fused append:", seed, cache, hq, hkv, d, ps, planned, groups, lens, flush=True)
+    w = _case("f32" if cache == "f32" else "bf16", cache, hq, hkv, d, seed=seed, lens=lens,
+              groups=groups)
+    k_new, v_new, slots = decode_new_tokens(w)
+    pool_a, pool_b = gpu_pool(w, without_new=True), gpu_pool(w, without_new=True)
+    pa_kv_append(k_new, v_new, pool_a.k, pool_a.v, slots, pool_a.k_scale, pool_a.v_scale)
+    want, parts_a = run_cascade(w, pool_a, ps, planned=planned)
+    got, parts_b = run_cascade(w, pool_b, ps, planned=planned, appended=(k_new, v_new, slots))
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a.k.view(torch.uint8), pool_b.k.view(torch.uint8))
+    assert torch.equal(pool_a.v.view(torch.uint8), pool_b.v.view(torch.uint8))
+    assert torch.equal(got, want)
+    for a, b in zip(parts_a, parts_b):
+        assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))

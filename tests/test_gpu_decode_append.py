@@ -283,3 +283,28 @@ def test_planned_launch_without_append_equals_pa_decode(cache, ps):
     if ps:
         for a, b in zip(parts_a, (pm, psum, po)):
             assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_append_seeded_random_configurations(seed):
+    """Seeded random shapes: cache type, head size, GQA shape, partition size
+    (single pass, or a multiple of 16 up to 1024), 1-48 sequences of 0-3000
+    positions.  The fused launch equals pa_kv_append + pa_decode bit for bit,
+    and the planned fused launch equals the unplanned one."""
+    rng = np.random.default_rng(2000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8)][int(rng.integers(6))]
+    d = [64, 128][int(rng.integers(2))]
+    lens = [int(x) for x in rng.integers(0, 3001, size=int(rng.integers(1, 49)))]
+    ps = 0 if int(rng.integers(6)) == 0 else 16 * int(rng.integers(1, 65))
+    print("fused append:", seed, cache, hq, hkv, d, ps, lens, flush=True)
+    w = build_workload("fr", seed=seed, device="cuda", q_dtype="f32" if cache == "f32" else "bf16",
+                       cache_dtype=cache, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                       decode_lens=lens)
+    want = _check(w, ps)
+    pool = gpu_pool(w, without_new=True)
+    got, _ = _run_planned(w, pool, ps, _plan_for(w, pool, ps))
+    full = gpu_pool(w)
+    assert torch.equal(pool.k.view(torch.uint8), full.k.view(torch.uint8))
+    assert torch.equal(pool.v.view(torch.uint8), full.v.view(torch.uint8))
+    assert torch.equal(got, want)
