@@ -223,3 +223,18 @@ def test_large_scores_stay_finite_and_exact(cache, ps):
     # fp32 score rounding is relative to the score: scaling Q by 64 scales the
     # absolute score error, hence the output error, by 64 as well
     _check(w, ps, tol=TOL[cache] * (64 if cache == "f32" else 1))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_seeded_random_configurations(seed):
+    """Seeded random shapes against the oracle: cache type, head size, GQA
+    shape (G = 1 .. 16, 3 included), 1-16 sequences of 0-3000 positions,
+    single pass or a partition size that is a multiple of 16 up to 1024."""
+    rng = np.random.default_rng(4000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8), (6, 2)][int(rng.integers(7))]
+    d = [64, 128][int(rng.integers(2))]
+    lens = [int(x) for x in rng.integers(0, 3001, size=int(rng.integers(1, 17)))]
+    ps = 0 if int(rng.integers(5)) == 0 else 16 * int(rng.integers(1, 65))
+    print("decode:", seed, cache, hq, hkv, d, ps, lens, flush=True)
+    _check(_case("f32" if cache == "f32" else "bf16", cache, hq, hkv, d, lens, seed=seed), ps)

@@ -266,3 +266,21 @@ def test_fused_append_seeded_random_configurations(seed):
     print("fused multi append:", seed, cache, hq, hkv, d, ps, chunks, flush=True)
     _fused_equals_separate(_case(cache, hq, hkv, d, chunks, seed=seed), ps,
                            bool(rng.integers(2)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_multi_query_seeded_random_configurations(seed):
+    """Seeded random shapes against the prefill oracle and the per-token
+    partitions: cache type, head size, GQA shape, 1-8 sequences of 1-64
+    query tokens over prefixes of 0-1500, partition sizes that are multiples
+    of 16 up to 512, planned or not."""
+    rng = np.random.default_rng(5000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8), (6, 2)][int(rng.integers(7))]
+    d = [64, 128][int(rng.integers(2))]
+    chunks = [(int(rng.integers(0, 1501)), int(rng.integers(1, 65)))
+              for _ in range(int(rng.integers(1, 9)))]
+    ps = 16 * int(rng.integers(1, 33))
+    planned = bool(rng.integers(2))
+    print("multi-query:", seed, cache, hq, hkv, d, ps, planned, chunks, flush=True)
+    _check(_case(cache, hq, hkv, d, chunks, seed=seed), ps, planned=planned)

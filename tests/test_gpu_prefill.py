@@ -160,3 +160,22 @@ def test_prefill_context_beyond_the_table_is_clamped(cache):
                      i32(w.chunk_block_tables), i32([200]), w.scale, pool.k_scale, pool.v_scale)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_seeded_random_configurations(seed):
+    """Seeded random shapes against the oracle: cache type, head size, GQA
+    shape, 1-6 chunks of 1-300 rows over prefixes of 0-1500."""
+    rng = np.random.default_rng(6000 + seed)
+    cache = ["f32", "bf16", "fp8"][int(rng.integers(3))]
+    hq, hkv = [(4, 4), (8, 2), (16, 2), (16, 1), (12, 4), (32, 8), (6, 2)][int(rng.integers(7))]
+    d = [64, 128][int(rng.integers(2))]
+    chunks = [(int(rng.integers(0, 1501)), int(rng.integers(1, 301)))
+              for _ in range(int(rng.integers(1, 7)))]
+    print("prefill:", seed, cache, hq, hkv, d, chunks, flush=True)
+    w = _case(cache, hq, hkv, d, chunks, seed=seed)
+    out = run_prefill(w, gpu_pool(w))
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(w)
+    err = max_abs_err(as_f64(out), _oracle(w, kp, vp))
+    assert err <= TOL[cache], err
