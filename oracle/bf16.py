@@ -19,4 +19,6 @@ def to_f64(bits):
     if b.dtype != np.uint16:
         raise TypeError("bf16 bit patterns must be uint16 or int16, got %s" % b.dtype)
     words = b.astype(np.uint32) << np.uint32(16)
-    return words.view(np.float32).astype(np.float64)
+    # signalling-NaN patterns widen to NaN; numpy would warn about the cast
+    with np.errstate(invalid="ignore"):
+        return words.view(np.float32).astype(np.float64)
