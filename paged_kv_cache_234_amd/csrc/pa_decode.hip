@@ -54,6 +54,7 @@
 namespace pa {
 
 constexpr int kMaxDecodeRows = 4096;
+constexpr int kStageRows = 34;          // split-K partial rows a plain wavefront collects in LDS (the most that fit)
 constexpr int kMaxMultiQuery = 64;     // query tokens per sequence in pa_decode_multi
 
 // Launch plan.  The decode prologue (row table, tile prefix, workgroup and
@@ -155,9 +156,11 @@ constexpr int kAppendCost = 1;
 // NC * 16 / G members or query positions.
 // PLAIN: sequence rows only (pa_decode); the group and multi-query row code
 // is compiled out.
-template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE, bool CI = false>
+// STAGE: the plain kernel's split-K rows collected in LDS (long ranges only)
+template <int KIND, int D, int NW, int NC, bool PLAIN, int MODE, bool CI = false, bool STAGE = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(waves_per_simd(KIND, D))))
 void decode_kernel(DecodeArgs a) {
+    static_assert(!STAGE || (PLAIN && D == 128 && MODE != kMakePlan), "staging: plain rows, head size 128");
     // which rows a plan describes: plain sequences, cascade or multi-query
     const int row_kind = PLAIN ? 0 : (a.query_start_loc != nullptr ? 2 : 1);
     using Ops = TileOps<KIND, D>;
@@ -1005,9 +1008,71 @@ void decode_kernel(DecodeArgs a) {
     float next_c = 0.f;
     int load_ord = 0, comp_ord = 0;
 
+    // Split-K partial rows written to HBM while the K/V stream runs cost
+    // far more than their bytes (the long-context batch's 17.6 MB of
+    // partials took about 40 us; the same stores into two lines that stay
+    // in L2 took nothing).  So launches whose wavefronts stream long ranges
+    // (STAGE) collect each wavefront's rows in LDS and write them when the
+    // area is full and once the range is done, two 512-byte rows per store
+    // instruction.  A short range (a few items) stores at once: held to its
+    // end, its rows would only lengthen the launch's tail.
+    constexpr bool kStage = STAGE;
+    constexpr int kStageMinTiles = 64;
+    const bool stage_on = kStage && ntiles >= kStageMinTiles;
+    f32x4* stage_o = nullptr;      // this wavefront's rows (kStageRows x D / 4)
+    long* stage_pi = nullptr;      // their partial indices
+    float* stage_ml = nullptr;     // their (m, l)
+    if constexpr (kStage) {
+        __shared__ f32x4 s_stage_o[NW][kStageRows * D / 4];
+        __shared__ long s_stage_pi[NW][kStageRows];
+        __shared__ float s_stage_ml[NW][kStageRows * 2];
+        stage_o = s_stage_o[wave];
+        stage_pi = s_stage_pi[wave];
+        stage_ml = s_stage_ml[wave];
+    }
+    int staged = 0;                // rows collected (the same in every lane)
+    auto flush_stage = [&]() {
+        if constexpr (kStage) {
+            for (int k = 0; k < staged; k += 2) {
+                const int row = k + (lane >> 5);
+                if (row < staged) {
+                    const f32x4 v = stage_o[row * (D / 4) + (lane & 31)];
+                    *reinterpret_cast<f32x4*>(a.part_out + stage_pi[row] * D + 4 * (lane & 31)) = v;
+                }
+            }
+            for (int row = lane; row < staged; row += kWave) {
+                a.part_max[stage_pi[row]] = stage_ml[2 * row];
+                a.part_sum[stage_pi[row]] = stage_ml[2 * row + 1];
+            }
+            staged = 0;
+        }
+    };
+
     // write an item's result from st: a split-K partial, or the output rows
     auto finish_item = [&](const Cursor& it) {
         const float vs = (KIND == kFP8) ? load_invariant(a.v_scale + it.h) : 1.0f;
+        if constexpr (kStage) {
+            if (a.split && stage_on) {
+                // plain rows: columns g < G hold the item's query heads
+                const int cols = a.group;
+                if (staged + cols > kStageRows) flush_stage();
+                const float lt = sum_over_groups(st.l[0]);
+                if (g < cols) {
+                    const int row = staged + g;
+                    const float inv = vs / lt;
+#pragma unroll
+                    for (int t = 0; t < NVT; ++t) stage_o[row * (D / 4) + 4 * t + grp] = st.o[0][t] * inv;
+                    if (grp == 0) {
+                        stage_pi[row] = ((long)col_seq[0] * a.num_heads + col_hq[0]) * a.max_partitions +
+                                        it.part;
+                        stage_ml[2 * row] = st.m[0] * kLn2;
+                        stage_ml[2 * row + 1] = lt * fast_exp2(st.mr[0] - st.m[0]);   // against the true max
+                    }
+                }
+                staged += cols;
+                return;
+            }
+        }
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
             const float lt = sum_over_groups(st.l[n]);      // against the reference mr
@@ -1276,8 +1341,13 @@ void decode_kernel(DecodeArgs a) {
                 break;
             }
         }
+        flush_stage();
     }
 }
+
+// Launches of plain rows at head size 128 whose bound on tiles per wavefront
+// reaches this take the kernel that collects split-K rows in LDS.
+constexpr long kStageBoundTiles = 128;
 
 template <int KIND, int D, int NC, bool PLAIN, int MODE = kRun, bool CI = false>
 static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t stream) {
@@ -1294,6 +1364,13 @@ static hipError_t launch_decode(const DecodeArgs& a, long max_tiles, hipStream_t
     if constexpr (PLAIN) grid = grid * 7 / 8;
     grid = std::min(grid, (max_tiles + NW - 1) / NW);
     grid = std::max(grid, 1L);
+    if constexpr (PLAIN && D == 128 && MODE != kMakePlan) {
+        if (a.split && max_tiles / (grid * NW) >= kStageBoundTiles) {
+            hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE, CI, true>),
+                               dim3((unsigned)grid), dim3(NW * kWave), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((decode_kernel<KIND, D, NW, NC, PLAIN, MODE, CI>), dim3((unsigned)grid), dim3(NW * kWave), 0,
                        stream, a);
     return hipGetLastError();
