@@ -1010,8 +1010,8 @@ void decode_kernel(DecodeArgs a) {
 
     // Split-K partial rows written to HBM while the K/V stream runs cost
     // far more than their bytes (the long-context batch's 17.6 MB of
-    // partials took about 40 us; the same stores into two lines that stay
-    // in L2 took nothing).  So launches whose wavefronts stream long ranges
+    // partials took about 40 us; the same stores into 2 KB that stays in
+    // L2 took nothing).  So launches whose wavefronts stream long ranges
     // (STAGE) collect each wavefront's rows in LDS and write them when the
     // area is full and once the range is done, two 512-byte rows per store
     // instruction.  A short range (a few items) stores at once: held to its
