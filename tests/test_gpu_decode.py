@@ -240,16 +240,20 @@ def test_decode_seeded_random_configurations(seed):
     _check(_case("f32" if cache == "f32" else "bf16", cache, hq, hkv, d, lens, seed=seed), ps)
 
 
-def test_split_k_rows_collected_in_lds_equal_direct_stores():
+@pytest.mark.parametrize("cache,hq,hkv,batch,pmax_big", [("bf16", 32, 8, 8, 128),
+                                                      ("bf16", 16, 1, 64, 128),
+                                                      ("fp8", 32, 8, 16, 256)])
+def test_split_k_rows_collected_in_lds_equal_direct_stores(cache, hq, hkv, batch, pmax_big):
     """Long ranges: a launch whose bound on tiles per wavefront is large
     collects each wavefront's split-K rows in LDS and writes them at the end
     of its range.  The bound follows max_partitions, so the same batch runs
-    both ways (79 partitions: direct stores; 128: collected); the partials
-    and outputs agree bit for bit."""
+    both ways (the partitions it needs: direct stores; pmax_big: collected);
+    the partials and outputs agree bit for bit.  G = 4 and 16 rows per item,
+    bf16 and fp8 caches."""
     from paged_kv_cache_234_amd import pa_decode
-    rng = np.random.default_rng(77)
-    lens = [int(x) for x in rng.integers(28000, 40001, size=8)]
-    w = _case("bf16", "bf16", 32, 8, 128, lens, seed=77)
+    rng = np.random.default_rng(77 + batch)
+    lens = [int(x) for x in rng.integers(28000, 40001, size=batch)]
+    w = _case("bf16", cache, hq, hkv, 128, lens, seed=77 + batch)
     pool = gpu_pool(w)
     q = w.q.contiguous()
     bt, cl = i32(w.block_tables), i32(w.context_lens)
@@ -257,17 +261,17 @@ def test_split_k_rows_collected_in_lds_equal_direct_stores():
     need = -(-max(lens) // 512)
     assert need < 80
     got = {}
-    for pmax in (need, 128):
+    for pmax in (need, pmax_big):
         pm = torch.full((B, hq, pmax), float("nan"), device="cuda")
         psum = torch.full_like(pm, float("nan"))
         po = torch.full((B, hq, pmax, d), float("nan"), device="cuda")
-        pa_decode(None, q, pool.k, pool.v, bt, cl, w.scale, partition_size=512, max_partitions=pmax,
-                  part_max=pm, part_sum=psum, part_out=po)
+        pa_decode(None, q, pool.k, pool.v, bt, cl, w.scale, pool.k_scale, pool.v_scale,
+                  partition_size=512, max_partitions=pmax, part_max=pm, part_sum=psum, part_out=po)
         out = torch.empty_like(q)
         pa_decode_splitk_reduce(out, pm, psum, po, cl, 512)
         torch.cuda.synchronize()
         got[pmax] = (out, pm[:, :, :need], psum[:, :, :need], po[:, :, :need])
-    a, b = got[need], got[128]
+    a, b = got[need], got[pmax_big]
     assert torch.equal(a[0], b[0])
     for x, y in zip(a[1:], b[1:]):
         assert torch.equal(x.nan_to_num(7.0), y.nan_to_num(7.0))
