@@ -26,8 +26,8 @@ class KVPool:
         x = 16 // torch.empty((), dtype=dt).element_size()
         # K and V share one allocation, K first.  Separate allocations land
         # wherever the driver puts them, and the decode reading block b of
-        # both at once ran slower: long-context batch (8 x 28-40k tokens,
-        # bf16) in a same-box A/B over eight processes, layer-step
+        # both at once ran slower: long-context batch (8 sequences, 537k
+        # tokens, bf16) in a same-box A/B over eight processes, layer-step
         # 360-364 us with one allocation against 365-370 us with two.
         n = num_blocks * num_kv_heads * head_dim * block_size
         self._kv = torch.empty(2 * n, dtype=dt, device=device)
