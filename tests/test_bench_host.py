@@ -99,3 +99,33 @@ def test_default_run_times_every_workload_with_the_long_context_headline():
     assert set(bench.GATE) <= set(names)
     assert args.cpu_seconds * len(names) <= 30          # a bounded CPU sample
     assert bench.parse(["--config", "4"]).workload == bench.HEADLINE
+
+
+@pytest.mark.parametrize("cache", ["f32", "bf16", "fp8"])
+def test_pool_k_and_v_share_one_allocation(cache):
+    """A pool's K and V are views of one allocation, V directly after K, in
+    the layouts the kernels take; the poison fills both, and filling K
+    leaves V untouched."""
+    import torch
+    from paged_kv_cache_234_amd import KVPool
+    nb, hkv, d = 5, 2, 64
+    p = KVPool(nb, hkv, d, cache, device="cpu")
+    x = 16 // p.k.element_size()
+    assert tuple(p.k.shape) == (nb, hkv, d // x, 16, x)
+    assert tuple(p.v.shape) == (nb, hkv, d, 16)
+    assert p.k.is_contiguous() and p.v.is_contiguous()
+    assert p.k.untyped_storage().data_ptr() == p.v.untyped_storage().data_ptr()
+    kbytes = p.k.numel() * p.k.element_size()
+    assert p.v.data_ptr() == p.k.data_ptr() + kbytes
+    assert p.k.untyped_storage().nbytes() == 2 * kbytes == p.nbytes()
+
+    def poisoned(t):
+        if cache == "f32":
+            return bool(torch.isnan(t).all())
+        if cache == "bf16":
+            return bool((t.view(torch.int16) == 0x7FC0).all())
+        return bool((t == 0x7F).all())
+
+    assert poisoned(p.k) and poisoned(p.v)
+    p.k.zero_()
+    assert poisoned(p.v) and not poisoned(p.k)
