@@ -329,6 +329,24 @@ class LayerStep:
                       pool.k_scale, pool.v_scale)
 
 
+def capture(body, stream):
+    """A HIP graph of the launches body() makes, captured on stream (a side
+    stream, not the current one) with capture_begin / capture_end.  The
+    torch.cuda.graph context manager would first hand every cached block
+    back to the driver, which moves where the next workload's pools land
+    (see the end of run_workload)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.capture_begin()
+        try:
+            body()
+        finally:
+            g.capture_end()
+    return g
+
+
 def run_workload(name, args, dev):
     """Time one workload; returns its record (all figures but the CPU legs)
     and the workload itself."""
@@ -364,11 +382,10 @@ def run_workload(name, args, dev):
         for i in range(count):
             fn(first + i, first)
 
+    capture_stream = torch.cuda.Stream()
+
     def captured(fn, first, count):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            steps_of(fn, first, count)
-        return g
+        return capture(lambda: steps_of(fn, first, count), capture_stream)
 
     if not args.eager:
         g_warm = captured(step, 0, warm)
@@ -509,7 +526,13 @@ def run_workload(name, args, dev):
     if not args.eager:
         del g_warm, g_steps, g_decode, g_prefill
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    # The freed memory stays in torch's cache for the next workload, as a
+    # serving process keeps its pools: handing it back to the driver (here,
+    # or on entry to each graph capture) made the pools allocated next land
+    # where the decode read them slower (long-context layer-step 359-360 ->
+    # 347-348 us, mixed fp8 178-179 -> 174-176 us, draft verification
+    # 53.6-53.7 -> 52.6-53.2 us, three same-box runs of every workload each
+    # way).
     return rec, w
 
 

@@ -44,10 +44,7 @@ def test_bench_step_full_size_every_row_every_replay(name):
     w, ps, spec = bench.make_workload(name, None, "cuda")
     ls = bench.LayerStep(w, ps, spec, "cuda", layer_copies=2, fill_new=False, poison=True)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for layer in range(3):
-            ls.step(layer, 0)
+    g = bench.capture(lambda: [ls.step(layer, 0) for layer in range(3)], torch.cuda.Stream())
     torch.cuda.synchronize()
 
     kp, vp = oracle_pool(w)
